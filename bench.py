@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of sliding-window attention with sinks on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only-main]
+
+One step = one banded prefill of the GQA Mistral-style workload (B=1, Hq=32,
+Hkv=8, d=128, L=8192, s=0, r=4096, bf16), inputs resident in HBM.  The JSON
+line's value is its algorithmic TFLOP/s: only the (query, key) pairs of the
+sink + window key set count, 4*d flops each.  Alongside it (under "extra")
+the same run times the StreamingLLM 4+1020 prefill (B=4, H=32, L=16384), the
+rolling-buffer decode loop (B=64, 32/8 heads, 4+4092 slots, append + decode
+per step) and the chunked RoPE streaming prefill (131072 tokens in chunks of
+4096).  The "cpu_baseline" leg times the fp64 oracle on a bounded sample of
+the main workload's rows.
+
+Prints exactly one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def key_count_sum(L: int, s: int, r: int, pos0: int = 0) -> int:
+    """sum over query rows t = pos0 .. pos0+L-1 of |U(t)| = min(t+1, s+r)."""
+    t = np.arange(pos0, pos0 + L, dtype=np.int64)
+    return int(np.minimum(t + 1, s + r).sum())
+
+
+def prefill_flops(w) -> float:
+    return 4.0 * w.d * key_count_sum(w.L, w.s, w.r) * w.B * w.Hq
+
+
+class LaunchTimer:
+    """HIP events around each launch, on the stream the kernels go to."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
+
+    def __enter__(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self._start = e
+        return self
+
+    def __exit__(self, *exc):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append((self._start, e))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+def to_dev(torch, x, dtype):
+    return torch.from_numpy(x).to("cuda").to(dtype).contiguous()
+
+
+def bench_prefill(torch, swa, w, steps, warmup):
+    q, k, v = __import__("swa_inputs").prefill_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = to_dev(torch, q, dt), to_dev(torch, k, dt), to_dev(torch, v, dt)
+    del q, k, v
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        swa.prefill(qd, kd, vd, w.s, w.r, out=out)
+    torch.cuda.synchronize()
+    timer = LaunchTimer(torch, stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        with timer:
+            swa.prefill(qd, kd, vd, w.s, w.r, out=out)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    flops = prefill_flops(w)
+    return {"ms": ms, "kernel_ms": timer.mean_ms(), "flops": flops, "tflops": flops / ms / 1e9}
+
+
+def bench_decode(torch, swa, w, steps=None):
+    si = __import__("swa_inputs")
+    steps = w.steps if steps is None else steps
+    hk, hv = si.decode_history(w)
+    kc, vc = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda")
+    hkd, hvd = to_dev(torch, hk, torch.bfloat16), to_dev(torch, hv, torch.bfloat16)
+    del hk, hv
+    swa.cache_append(hkd, hvd, kc, vc, 0, w.s, w.r)
+    torch.cuda.synchronize()
+    del hkd, hvd
+    qs, ks, vs = si.decode_steps(w, steps=steps)
+    qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (qs, ks, vs))
+    del qs, ks, vs
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+    desc = swa.make_desc(w.B, w.Hq, w.Hkv, w.d, w.s, w.r, torch.bfloat16)
+    ws = torch.empty(swa.decode_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    kn = [kd[i].unsqueeze(2) for i in range(steps)]
+    vn = [vd[i].unsqueeze(2) for i in range(steps)]
+    # warm-up on a copy of the cache state would change T; run 8 steps on a
+    # scratch cache instead
+    kc2, vc2 = kc.clone(), vc.clone()
+    for i in range(8):
+        swa.cache_append(kn[i], vn[i], kc2, vc2, w.L + i, w.s, w.r)
+        swa.decode(qd[i], kc2, vc2, w.L + i + 1, w.s, w.r, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    del kc2, vc2
+    timer = LaunchTimer(torch, stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        T = w.L + i + 1
+        swa.cache_append(kn[i], vn[i], kc, vc, T - 1, w.s, w.r)
+        with timer:
+            swa.decode(qd[i], kc, vc, T, w.s, w.r, out=out, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    S = w.s + w.r
+    kv = w.B * w.Hkv * S * w.d * 2 * 2
+    qo = 2 * w.B * w.Hq * w.d * 2
+    app = w.B * w.Hkv * w.d * 2 * 2
+    step_bytes = kv + qo + app
+    return {"ms": ms, "decode_ms": timer.mean_ms(), "bytes_per_step": step_bytes,
+            "gbs": step_bytes / ms / 1e6, "decode_kernel_bytes": kv + qo}
+
+
+def bench_chunked(torch, swa, w, reps=2):
+    si = __import__("swa_inputs")
+    q, k, v = si.chunk_inputs(w, 0, w.L)
+    qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
+    del q, k, v
+    C = w.chunk
+    chunks = [(p0, min(w.L, p0 + C)) for p0 in range(0, w.L, C)]
+    parts = [tuple(x[:, :, a:b].contiguous() for x in (qd, kd, vd)) for a, b in chunks]
+    out = torch.empty_like(qd[:, :, :C])
+    desc = swa.make_desc(w.B, w.Hq, w.Hkv, w.d, w.s, w.r, torch.bfloat16, rope_base=w.rope_base)
+    ws = torch.empty(max(16, swa.prefill_workspace_bytes(desc, C)), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one_pass(timer=None):
+        kc, vc = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda")
+        for (a, b), (qc, kk, vv) in zip(chunks, parts):
+            o = out[:, :, :b - a]
+            if timer is not None:
+                with timer:
+                    swa.prefill(qc, kk, vv, w.s, w.r, rope_base=w.rope_base, k_cache=kc if a else None,
+                                v_cache=vc if a else None, pos0=a, out=o, workspace=ws)
+            else:
+                swa.prefill(qc, kk, vv, w.s, w.r, rope_base=w.rope_base, k_cache=kc if a else None,
+                            v_cache=vc if a else None, pos0=a, out=o, workspace=ws)
+            swa.cache_append(kk, vv, kc, vc, a, w.s, w.r)
+
+    one_pass()
+    torch.cuda.synchronize()
+    timer = LaunchTimer(torch, stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        one_pass(timer)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    flops = 4.0 * w.d * key_count_sum(w.L, w.s, w.r) * w.B * w.Hq
+    return {"ms": ms, "flops": flops, "tflops": flops / ms / 1e9, "prefill_call_ms": timer.mean_ms()}
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle, as it stands, on random rows of the main workload."""
+    import oracle
+    import swa_inputs as si
+    q, k, v = si.prefill_inputs(w)
+    g = np.random.default_rng(99)
+    done_rows, done_keys, elapsed = 0, 0, 0.0
+    batch = 512
+    while elapsed < budget_s:
+        rows = np.stack([g.integers(0, w.B, batch), g.integers(0, w.Hq, batch), g.integers(0, w.L, batch)], axis=1)
+        t0 = time.perf_counter()
+        _, nk = oracle.prefill_rows(q, k, v, w.s, w.r, rows=rows, return_nkeys=True)
+        elapsed += time.perf_counter() - t0
+        done_rows += batch
+        done_keys += int(nk.sum())
+        batch = min(batch * 2, 16384)
+    flops = 4.0 * w.d * done_keys
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "%d random query rows of %s (%d keys), fp64, %.1f s" % (done_rows, w.name, done_keys, elapsed)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-main", action="store_true", help="time the main workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sliding_window_attention_sink_amd as swa
+    import swa_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    swa.load()
+
+    w = si.WORKLOADS[2]
+    log("main workload", w.name)
+    main_res = bench_prefill(torch, swa, w, args.steps, args.warmup)
+    log("main", main_res)
+
+    extra = {}
+    if not args.only_main:
+        w3 = si.WORKLOADS[3]
+        r3 = bench_prefill(torch, swa, w3, max(5, args.steps // 2), 2)
+        extra[w3.name] = {"tflops": r3["tflops"], "ms": r3["ms"], "kernel_ms": r3["kernel_ms"],
+                          "frac_bf16_peak": r3["tflops"] / PEAK_BF16_TFLOPS}
+        log("w3", r3)
+        torch.cuda.empty_cache()
+        w4 = si.WORKLOADS[4]
+        r4 = bench_decode(torch, swa, w4)
+        dec_gbs = r4["decode_kernel_bytes"] / r4["decode_ms"] / 1e6
+        extra[w4.name] = {"GB/s": r4["gbs"], "us_per_step": r4["ms"] * 1e3, "steps": w4.steps,
+                          "bytes_per_step": r4["bytes_per_step"], "frac_hbm_peak": r4["gbs"] / PEAK_HBM_GBS,
+                          "decode_launch_us": r4["decode_ms"] * 1e3, "decode_launch_GB/s": dec_gbs,
+                          "decode_launch_frac_hbm_peak": dec_gbs / PEAK_HBM_GBS}
+        log("w4", r4)
+        torch.cuda.empty_cache()
+        w5 = si.WORKLOADS[5]
+        r5 = bench_chunked(torch, swa, w5)
+        extra[w5.name] = {"tflops": r5["tflops"], "ms": r5["ms"], "frac_bf16_peak": r5["tflops"] / PEAK_BF16_TFLOPS,
+                          "prefill_call_ms": r5["prefill_call_ms"]}
+        log("w5", r5)
+        torch.cuda.empty_cache()
+        w1 = si.WORKLOADS[1]
+        r1 = bench_prefill(torch, swa, w1, 20, 3)
+        extra[w1.name] = {"tflops": r1["tflops"], "ms": r1["ms"], "frac_f32_peak": r1["tflops"] / PEAK_F32_TFLOPS}
+
+    achieved = main_res["flops"] / main_res["kernel_ms"] / 1e9
+    line = {
+        "metric": "SWA+sink prefill TFLOP/s and decode KV GB/s, % of roofline, 1 MI355X",
+        "value": main_res["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L, "s": w.s, "r": w.r,
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<bf16,128>", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * swa.h - C ABI of the MI355X (gfx950) sliding-window attention library.
+ *
+ * The operation: causal softmax attention in which query t attends the first
+ * s tokens (attention sinks) and its r most recent tokens including itself,
+ * each key once,
+ *     U(t) = { i <= t : i < s or i >= t - r + 1 },   |U(t)| = min(t+1, s+r),
+ *     O_t  = sum_{i in U(t)} softmax_i(scale * q_t . k_i) v_i .
+ * Sources: the SWA formula and the fixed first s = 4 sink tokens in the
+ * "带 Sink 的滑动窗口注意力" section of the hyper.ai summary of arXiv
+ * 2608.28444; the sink + recent cache composition (eq:attn-fixed-streaming),
+ * the rolling buffer (eq:attn-fixed-rolling), chunked prefill and RoPE
+ * re-positioning inside the cache on the t6page page "滑窗与固定稀疏";
+ * softmax attention, eq.(1) of section 2.1 of the Blurry Window Attention
+ * page (arXiv 2606.09862).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays
+ *    whose base address is 16-byte aligned.  Element type is desc->dtype
+ *    (fp32 or bf16); the output has the input's type.  The caller owns every
+ *    buffer (inputs, outputs, caches, workspaces); the library never
+ *    allocates, frees or synchronises.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    kernels on it and return; device-side results are ready after the
+ *    caller synchronises the stream.
+ *  - Return value: SWA_OK (0) or a negative status.  Arguments are validated
+ *    on the host before any HIP call; a rejected call enqueues nothing and
+ *    leaves a message in swa_last_error() (per calling thread).
+ *  - GQA: q-head h reads kv-head h / (Hq / Hkv) (contiguous groups).
+ *  - Rolling cache layout [B, Hkv, s + r, d]: token p lives in slot p when
+ *    p < s, else in slot s + (p mod r) (the sink slots in front of an r-slot
+ *    rolling buffer written at p mod r).  Tokens below s go only to their
+ *    sink slot.
+ */
+#ifndef SWA_H_
+#define SWA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWA_ABI_VERSION 1
+
+enum swa_status {
+    SWA_OK = 0,
+    SWA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misalignment, workspace too small */
+    SWA_ERR_UNSUPPORTED = -2,  /* valid but not built: d not in {64, 128}, unknown dtype */
+    SWA_ERR_HIP = -3           /* a HIP launch or runtime call failed */
+};
+
+enum swa_dtype { SWA_F32 = 0, SWA_BF16 = 1 };
+
+typedef struct swa_desc {
+    int32_t B;          /* batch (sequences), >= 1 */
+    int32_t Hq;         /* query heads, >= 1 */
+    int32_t Hkv;        /* key/value heads, >= 1, divides Hq */
+    int32_t d;          /* head dimension: 64 or 128 */
+    int32_t s;          /* sink tokens, >= 0 */
+    int32_t r;          /* recent tokens including the query's own, >= 1 */
+    int32_t dtype;      /* enum swa_dtype */
+    float scale;        /* score scale, > 0 (usually 1/sqrt(d)) */
+    float rope_base;    /* 0: no rotary embedding; > 0: RoPE base (bf16 only) */
+} swa_desc;
+
+/*
+ * Bytes of device workspace swa_prefill needs for these arguments.  Zero
+ * without RoPE.  With RoPE (rope_base > 0) the keys of the cache and of the
+ * chunk and the chunk's queries are rotated once per call into the
+ * workspace: (2 * B*Hq*L + B*Hkv*(s + r + L)) * d * 2 bytes, rounded up.
+ */
+size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L);
+
+/*
+ * Banded flash-style prefill of L query rows.
+ *   q, o: [B, Hq, L, d];  k, v: [B, Hkv, L, d]  (the chunk's own tokens).
+ * Plain prefill: k_cache = v_cache = NULL and pos0 = 0; row i is position i.
+ * Chunked prefill: rows are positions pos0 .. pos0+L-1, and k_cache/v_cache
+ * ([B, Hkv, s + r, d], the rolling cache) hold tokens 0 .. pos0-1 written by
+ * swa_cache_append; the cache is read, not written (append the chunk after
+ * this call, on the same stream).  pos0 > 0 requires a cache.
+ * RoPE (desc->rope_base > 0): keys and values are stored before rotation;
+ * for each query the keys of U(t) in temporal order sit at positions
+ * 0 .. |U(t)|-1 and the query at |U(t)|-1 (positions re-assigned inside the
+ * cache, t6page StreamingLLM paragraph).  Rotation pairs dimension j with
+ * j + d/2, angle position * rope_base^(-2j/d).  Needs a workspace of
+ * swa_prefill_workspace_bytes() bytes; otherwise workspace may be NULL.
+ * Errors: SWA_ERR_INVALID_ARG (null or misaligned pointer, L < 1, pos0 < 0,
+ * pos0 > 0 without a cache, workspace too small, s < 0, r < 1, Hq % Hkv,
+ * scale <= 0), SWA_ERR_UNSUPPORTED (d, dtype, RoPE with fp32), SWA_ERR_HIP.
+ */
+int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
+                const void* k_cache, const void* v_cache, int64_t pos0,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Write tokens pos0 .. pos0+n-1 (k_new, v_new: [B, Hkv, n, d]) into the
+ * rolling cache (k_cache, v_cache: [B, Hkv, s + r, d]) at their slots.  When
+ * n > r several tokens of the call map to one recent slot; only the last of
+ * them (the one that survives in a token-by-token append) is written, so
+ * every slot has one writer.  Bytes are copied unchanged.
+ * Errors: SWA_ERR_INVALID_ARG (null/misaligned pointer, n < 1, pos0 < 0,
+ * bad shape fields), SWA_ERR_UNSUPPORTED (d, dtype), SWA_ERR_HIP.
+ */
+int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new, int64_t n, int64_t pos0,
+                     void* k_cache, void* v_cache, void* stream);
+
+/*
+ * Split-K decode.  Bytes of workspace swa_decode needs for n_split splits of
+ * the s + r slots (0 = the library's choice for this shape):
+ * B * Hq * n_split * (d + 2) * 4 bytes.
+ */
+size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split);
+
+/*
+ * One decode step: the query q ([B, Hq, d]) of the token at position T-1
+ * attends the cache ([B, Hkv, s + r, d]) holding tokens 0 .. T-1 (append the
+ * token first), i.e. U(T-1).  Slot order does not matter to softmax
+ * attention over a set, so slots are read in physical order.  Writes
+ * o ([B, Hq, d]).  n_split: 0 = the library's choice, else 1 .. 64.
+ * Errors: SWA_ERR_INVALID_ARG (null/misaligned pointer, T < 1, workspace too
+ * small, n_split out of range), SWA_ERR_UNSUPPORTED (d, dtype other than
+ * bf16, RoPE), SWA_ERR_HIP.
+ */
+int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const void* v_cache, int64_t T,
+               void* o, int32_t n_split, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The split count swa_decode uses for n_split = 0. */
+int32_t swa_decode_default_splits(const swa_desc* desc);
+
+/* Static text for a status code. */
+const char* swa_status_str(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* swa_last_error(void);
+
+/* SWA_ABI_VERSION of the loaded library. */
+int swa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H_ */

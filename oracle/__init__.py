@@ -14,4 +14,5 @@ from .oracle import (  # noqa: F401
     library_path,
     prefill_rows,
     rope,
+    threads,
 )

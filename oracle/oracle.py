@@ -51,6 +51,8 @@ def _load():
         lib.swa_oracle_rope.argtypes = [vp, vp, i64, i64, f64]
         lib.swa_oracle_key_set.restype = i64
         lib.swa_oracle_key_set.argtypes = [i64, i64, i64, vp]
+        lib.swa_oracle_threads.restype = ctypes.c_int
+        lib.swa_oracle_threads.argtypes = []
         _lib = lib
     return _lib
 
@@ -61,6 +63,11 @@ def _f32(x):
 
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's row loop runs on."""
+    return int(_load().swa_oracle_threads())
 
 
 def key_set(t: int, s: int, r: int) -> np.ndarray:

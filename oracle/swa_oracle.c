@@ -34,6 +34,7 @@
  * All arithmetic is fp64; inputs are the float32 values the device receives.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -222,3 +223,6 @@ int64_t swa_oracle_key_set(int64_t t, int64_t s, int64_t r, int64_t* keys) {
     if (t < 0 || s < 0 || r < 1 || !keys) return ORACLE_EINVAL;
     return key_set(t, s, r, keys);
 }
+
+/* Threads the parallel loops use (the CPU-baseline leg reports it). */
+int swa_oracle_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,22 @@
+"""Sliding-window softmax attention with attention sinks on MI355X (gfx950).
+
+The computation lives in libswa.so (hand-written HIP kernels behind the C ABI
+of include/swa.h); this package binds it for PyTorch callers:
+
+  * prefill(q, k, v, s, r, ...)        banded flash-style prefill, optional
+                                       rolling cache (chunked) and RoPE
+  * cache_append(k, v, kc, vc, pos0, ...) write tokens into the rolling cache
+  * decode(q, kc, vc, T, s, r, ...)    split-K single-query decode
+
+The low-level same-name wrappers of the C functions are in ``_lib``.
+"""
+from ._lib import EXPORTS, LIB_PATH, SwaDesc, SwaError, load  # noqa: F401
+from .ops import (  # noqa: F401
+    cache_append,
+    decode,
+    decode_workspace_bytes,
+    make_desc,
+    new_cache,
+    prefill,
+    prefill_workspace_bytes,
+)

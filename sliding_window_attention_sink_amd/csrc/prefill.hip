@@ -1,0 +1,445 @@
+// Banded flash-style prefill for sliding-window attention with sinks, gfx950.
+//
+// Row t attends U(t) = {i <= t : i < s or i >= t - r + 1} (sinks plus the r
+// most recent keys, each once; hyper.ai summary of arXiv 2608.28444, section
+// "带 Sink 的滑动窗口注意力", and eq:attn-fixed-streaming on the t6page page
+// "滑窗与固定稀疏").  The mask is fixed by position, so whole tiles outside
+// the band are never loaded (the "zero scoring cost, regular banded access"
+// argument of the fixed-sparsity section of that page).
+//
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one q-head):
+//  * key tiles of 64 positions are staged in LDS; a phase is a range of tiles
+//    with a mask rule: the sink phase (keys < s, visited once per query tile)
+//    and the band phase (keys >= max(s, t - r + 1)); without RoPE the two
+//    merge when they touch, with the single mask "i < s or i >= t - r + 1";
+//  * each wave owns 32 query rows and skips 32-key blocks that are masked for
+//    all of them;
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (fp32: v_mfma_f32_32x32x2_f32):
+//    the accumulator gives every lane one query row (lanes l and l+32 share
+//    it), so the row max needs one cross-lane exchange and the row sum none
+//    until the end;
+//  * online softmax in fp32 on exp2 with scale*log2(e) folded in; the running
+//    max is only raised when a block's max exceeds it by more than 2^8, which
+//    keeps O's rescaling rare and the result exact (the same max enters the
+//    numerator and the denominator);
+//  * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
+//    accumulator (rows of K are fed to the MFMA in a permuted order so each
+//    lane's eight P values are eight consecutive keys), V is transposed into
+//    LDS so that those eight keys are one 16-byte read.
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int NW = 4;            // waves per workgroup
+constexpr int WROWS = 32;        // query rows per wave
+constexpr int BM = NW * WROWS;   // query rows per workgroup
+static_assert(BM == kPrefillRowsPerBlock, "host tiling must match");
+constexpr int BN = 64;           // key positions per LDS tile
+constexpr int NT = NW * 64;      // threads per workgroup
+constexpr float RESCALE_TH = 8.0f;  // log2 units: raise the running max only past 2^8
+constexpr int NO_BAND = 0x7fffffff;
+
+// MFMA row rho of a 32-key block holds key swap23(rho) (bits 2 and 3 swapped).
+// With that order the 32x32 accumulator element i of lane group g holds key
+// 16*(i/8) + 8*g + (i%8): eight consecutive keys per PV k-step.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+__device__ __forceinline__ constexpr int keyoff(int i, int g) { return 16 * (i / 8) + 8 * g + (i % 8); }
+
+struct Phase {
+    int first, last;     // tile indices, inclusive
+    int sink_hi;         // keys < sink_hi are sinks
+    int band_lo;         // band keys are >= max(band_lo, t - r + 1)
+    int use_qs;          // read the sink queries
+};
+
+template <typename T, int D>
+struct Tiles;
+
+// ---------------------------------------------------------------- bf16 tiles
+template <int D>
+struct Tiles<__bf16, D> {
+    static constexpr int CH = D / 8;                    // 16-byte chunks per key row
+    static constexpr int K_LD = BN * CH / NT;           // K chunks per thread
+    static constexpr int V_TASKS = (BN / 4) * CH;       // (4 keys x 8 dims) blocks per tile
+    static constexpr int QK_STEPS = D / 16;
+    struct Smem {
+        u32x4 k[BN * CH];          // [key][chunk ^ swz_k(key)]
+        u32x4 vt[D * (BN / 8)];    // [dim][8-key chunk ^ swz_v(dim)]
+    };
+    struct Regs { u32x4 k[K_LD]; u32x4 v[4]; };
+    typedef bf16x8 QReg;
+    static constexpr int QREGS = QK_STEPS;
+
+    static __device__ __forceinline__ int swz_k(int key) { return swap23(key & 15) & (CH - 1); }
+    static __device__ __forceinline__ int swz_v(int dim) { return (dim ^ (dim >> 3)) & 7; }
+
+    template <class KPtr, class VPtr, class Loadable>
+    static __device__ __forceinline__ void load(Regs& R, int kbase, int tid, KPtr kptr, VPtr vptr,
+                                                Loadable ok) {
+#pragma unroll
+        for (int ld = 0; ld < K_LD; ++ld) {
+            int idx = ld * NT + tid;
+            int key = idx / CH, c = idx % CH;
+            int p = kbase + key;
+            R.k[ld] = ok(p) ? *(const u32x4*)(kptr(p) + c * 8) : u32x4{0, 0, 0, 0};
+        }
+        if (tid < V_TASKS) {
+            int kq = tid / CH, dc = tid % CH;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int p = kbase + 4 * kq + j;
+                R.v[j] = ok(p) ? *(const u32x4*)(vptr(p) + dc * 8) : u32x4{0, 0, 0, 0};
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void store(Smem& S, const Regs& R, int tid) {
+#pragma unroll
+        for (int ld = 0; ld < K_LD; ++ld) {
+            int idx = ld * NT + tid;
+            int key = idx / CH, c = idx % CH;
+            S.k[key * CH + (c ^ swz_k(key))] = R.k[ld];
+        }
+        if (tid < V_TASKS) {
+            int kq = tid / CH, dc = tid % CH;
+            // 4 keys x 8 dims -> 8 dims x 4 keys
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                const int w = e >> 1;
+                u32x2 cell;
+                cell[0] = __builtin_amdgcn_perm(R.v[1][w], R.v[0][w], sel);
+                cell[1] = __builtin_amdgcn_perm(R.v[3][w], R.v[2][w], sel);
+                int dim = dc * 8 + e;
+                int chunk = (kq >> 1) ^ swz_v(dim);
+                ((u32x2*)S.vt)[(dim * (BN / 8) + chunk) * 2 + (kq & 1)] = cell;
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void load_q(QReg* q, const __bf16* row, bool valid, int g) {
+#pragma unroll
+        for (int ks = 0; ks < QK_STEPS; ++ks) {
+            u32x4 x = valid ? *(const u32x4*)(row + 16 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+            q[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+
+    // S^T block (32 keys x 32 rows) of half-block hb.
+    static __device__ __forceinline__ f32x16 qk(const Smem& S, const QReg* q, int hb, int l32, int g) {
+        f32x16 acc = {};
+        const int key = hb * 32 + swap23(l32);
+        const int sw = swz_k(key);
+#pragma unroll
+        for (int ks = 0; ks < QK_STEPS; ++ks) {
+            bf16x8 a = __builtin_bit_cast(bf16x8, S.k[key * CH + ((2 * ks + g) ^ sw)]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], acc, 0, 0, 0);
+        }
+        return acc;
+    }
+
+    // O^T += V^T P^T for half-block hb; p holds exp'd scores in accumulator order.
+    static __device__ __forceinline__ void pv(const Smem& S, const float* p, f32x16* o, int hb, int l32, int g) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = (__bf16)p[8 * kk + e];
+            const int c16 = 4 * hb + 2 * kk + g;   // 16-byte chunk of 8 keys in a V^T row
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const int dim = 32 * db + l32;
+                const int chunk = c16 ^ swz_v(dim);
+                const u32x4 x = S.vt[dim * (BN / 8) + chunk];
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), b, o[db], 0, 0, 0);
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void store_o(__bf16* row, const f32x16* o, float inv, int g) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                __bf16 v0 = (__bf16)(o[db][4 * q4 + 0] * inv);
+                __bf16 v1 = (__bf16)(o[db][4 * q4 + 1] * inv);
+                __bf16 v2 = (__bf16)(o[db][4 * q4 + 2] * inv);
+                __bf16 v3 = (__bf16)(o[db][4 * q4 + 3] * inv);
+                u32x2 w;
+                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
+                *(u32x2*)(row + 32 * db + 8 * q4 + 4 * g) = w;
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------- fp32 tiles
+template <int D>
+struct Tiles<float, D> {
+    static constexpr int CH = D / 4;                    // 16-byte chunks per key row
+    static constexpr int LD = BN * CH / NT;             // chunks per thread (K and V each)
+    static constexpr int KS = D + 1;                    // padded K row stride (floats)
+    static constexpr int QK_STEPS = D / 2;
+    struct Smem {
+        float k[BN * KS];
+        float v[BN * D];
+    };
+    struct Regs { u32x4 k[LD]; u32x4 v[LD]; };
+    typedef float QReg;
+    static constexpr int QREGS = QK_STEPS;
+
+    template <class KPtr, class VPtr, class Loadable>
+    static __device__ __forceinline__ void load(Regs& R, int kbase, int tid, KPtr kptr, VPtr vptr,
+                                                Loadable ok) {
+#pragma unroll
+        for (int ld = 0; ld < LD; ++ld) {
+            int idx = ld * NT + tid;
+            int key = idx / CH, c = idx % CH;
+            int p = kbase + key;
+            bool y = ok(p);
+            R.k[ld] = y ? *(const u32x4*)(kptr(p) + c * 4) : u32x4{0, 0, 0, 0};
+            R.v[ld] = y ? *(const u32x4*)(vptr(p) + c * 4) : u32x4{0, 0, 0, 0};
+        }
+    }
+
+    static __device__ __forceinline__ void store(Smem& S, const Regs& R, int tid) {
+#pragma unroll
+        for (int ld = 0; ld < LD; ++ld) {
+            int idx = ld * NT + tid;
+            int key = idx / CH, c = idx % CH;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S.k[key * KS + 4 * c + e] = __builtin_bit_cast(float, R.k[ld][e]);
+            *(u32x4*)&S.v[key * D + 4 * c] = R.v[ld];
+        }
+    }
+
+    static __device__ __forceinline__ void load_q(QReg* q, const float* row, bool valid, int g) {
+#pragma unroll
+        for (int ks = 0; ks < QK_STEPS; ++ks) q[ks] = valid ? row[2 * ks + g] : 0.0f;
+    }
+
+    static __device__ __forceinline__ f32x16 qk(const Smem& S, const QReg* q, int hb, int l32, int g) {
+        f32x16 acc = {};
+        const float* krow = &S.k[(hb * 32 + swap23(l32)) * KS];
+#pragma unroll
+        for (int ks = 0; ks < QK_STEPS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + g], q[ks], acc, 0, 0, 0);
+        return acc;
+    }
+
+    static __device__ __forceinline__ void pv(const Smem& S, const float* p, f32x16* o, int hb, int l32, int g) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float* vrow = &S.v[(hb * 32 + keyoff(i, g)) * D];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * db + l32], p[i], o[db], 0, 0, 0);
+        }
+    }
+
+    static __device__ __forceinline__ void store_o(float* row, const f32x16* o, float inv, int g) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float4 w = make_float4(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv, o[db][4 * q4 + 2] * inv,
+                                       o[db][4 * q4 + 3] * inv);
+                *(float4*)(row + 32 * db + 8 * q4 + 4 * g) = w;
+            }
+        }
+    }
+};
+
+// Maps blockIdx to a work item so that each XCD (blocks are dealt to the 8
+// XCDs round-robin) gets one contiguous run of work items: neighbouring query
+// tiles of a head, which read overlapping key tiles, then share that XCD's L2.
+__device__ __forceinline__ int xcd_work_item(int bid, int nblk) {
+    const int x = bid & 7, k = bid >> 3;
+    const int per = nblk >> 3, rem = nblk & 7;
+    return x * per + (x < rem ? x : rem) + k;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
+    typedef Tiles<T, D> TL;
+    __shared__ typename TL::Smem smem;
+
+    const int w = xcd_work_item(blockIdx.x, gridDim.x);
+    const int mt = a.n_mtiles - 1 - (w % a.n_mtiles);   // late (heavier) query tiles first
+    const int bh = w / a.n_mtiles;
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int kvh = h / (a.Hq / a.Hkv);
+    const int s = a.s, r = a.r;
+    const int pos0 = (int)a.pos0;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, g = lane >> 5;
+
+    const int row0 = mt * BM;                                   // first row of the tile (call-relative)
+    const int nrows = (int)((a.L - row0) < BM ? (a.L - row0) : BM);
+    const int t0 = pos0 + row0, t1 = t0 + nrows - 1;            // positions of the tile's rows
+    const int tw0 = t0 + wave * WROWS;
+    const int tw1 = (tw0 + WROWS - 1) < t1 ? (tw0 + WROWS - 1) : t1;
+    const bool wave_active = tw0 <= t1;
+    const int my_t = tw0 + l32;
+    const bool my_valid = my_t <= t1;
+
+    const size_t qoff = ((size_t)bh * a.L + row0 + wave * WROWS + l32) * D;
+    const T* kn = (const T*)a.kn + (size_t)(b * a.Hkv + kvh) * a.L * D;
+    const T* vn = (const T*)a.vn + (size_t)(b * a.Hkv + kvh) * a.L * D;
+    const T* kc = a.kc ? (const T*)a.kc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
+    const T* vc = a.vc ? (const T*)a.vc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
+
+    auto kptr = [&](int p) -> const T* {
+        if (p >= pos0) return kn + (size_t)(p - pos0) * D;
+        int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
+        return kc + (size_t)sl * D;
+    };
+    auto vptr = [&](int p) -> const T* {
+        if (p >= pos0) return vn + (size_t)(p - pos0) * D;
+        int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
+        return vc + (size_t)sl * D;
+    };
+
+    // ---- phases (uniform over the workgroup)
+    Phase ph0 = {0, -1, 0, NO_BAND, 0}, ph1 = {0, -1, 0, NO_BAND, 0};
+    int nph = 0;
+    {
+        const int sink_end = s < t1 + 1 ? s : t1 + 1;           // keys [0, sink_end) are sinks
+        const int band_lo = s > t0 - r + 1 ? s : t0 - r + 1;    // lowest band key of the tile
+        const bool has_sink = sink_end > 0, has_band = band_lo <= t1;
+        const int st_last = has_sink ? (sink_end - 1) / BN : -1;
+        const int bt_first = band_lo / BN, bt_last = t1 / BN;
+        const Phase sink_ph = {0, st_last, s, NO_BAND, 1};
+        const Phase band_ph = {bt_first, bt_last, 0, s, 0};
+        if (a.merge_sink && has_sink && has_band && bt_first <= st_last + 1) {
+            ph0 = Phase{0, bt_last, s, s, 0};
+            nph = 1;
+        } else if (has_sink) {
+            ph0 = sink_ph;
+            ph1 = band_ph;
+            nph = has_band ? 2 : 1;
+        } else if (has_band) {
+            ph0 = band_ph;
+            nph = 1;
+        }
+    }
+
+    typename TL::QReg qreg[TL::QREGS];
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    float m_c = -__builtin_inff();   // running max in scale*log2e units
+    float l_part = 0.0f;             // this lane's share of the row sum
+    const float c = a.scale_log2e;
+
+    typename TL::Regs regs;
+    int q_loaded = -1;
+    for (int pi = 0; pi < nph; ++pi) {
+        const Phase P = pi ? ph1 : ph0;
+        // a key position is loaded iff some row of this tile needs it
+        const int lo_any = P.band_lo > t0 - r + 1 ? P.band_lo : t0 - r + 1;
+        auto loadable = [&](int p) { return p <= t1 && (p < P.sink_hi || p >= lo_any); };
+
+        const int want_q = (P.use_qs && a.qs != a.q) ? 1 : 0;
+        if (want_q != q_loaded) {
+            const T* qsrc = (const T*)(want_q ? a.qs : a.q) + qoff;
+            TL::load_q(qreg, qsrc, my_valid, g);
+            q_loaded = want_q;
+        }
+
+        TL::load(regs, P.first * BN, tid, kptr, vptr, loadable);
+        for (int j = P.first; j <= P.last; ++j) {
+            __syncthreads();
+            TL::store(smem, regs, tid);
+            __syncthreads();
+            if (j < P.last) TL::load(regs, (j + 1) * BN, tid, kptr, vptr, loadable);
+            if (!wave_active) continue;
+
+            const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
+            const int lo_w1 = P.band_lo > tw1 - r + 1 ? P.band_lo : tw1 - r + 1;
+            const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int kb = j * BN + hb * 32;
+                const bool need = kb <= tw1 && (kb < P.sink_hi || kb + 31 >= lo_w0);
+                if (!need) continue;
+                const bool full = kb + 31 <= tw0 && (kb >= lo_w1 || kb + 31 < P.sink_hi);
+
+                f32x16 sacc = TL::qk(smem, qreg, hb, l32, g);
+                if (!full) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb + keyoff(i, g);
+                        const bool ok = key <= my_t && (key < P.sink_hi || key >= lo_me);
+                        sacc[i] = ok ? sacc[i] : -__builtin_inff();
+                    }
+                }
+                float mx = sacc[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+                {
+                    auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                               __builtin_bit_cast(uint32_t, mx), false, false);
+                    mx = fmaxf(mx, fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
+                                         __builtin_bit_cast(float, (uint32_t)sw[1])));
+                }
+                const float mxc = mx * c;
+                const bool upd = mxc > m_c + RESCALE_TH;
+                if (__builtin_amdgcn_ballot_w64(upd)) {
+                    const float alpha = upd ? __builtin_amdgcn_exp2f(m_c - mxc) : 1.0f;
+                    m_c = upd ? mxc : m_c;
+                    l_part *= alpha;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+                }
+                const float mneg = (m_c == -__builtin_inff()) ? 0.0f : -m_c;
+                float p[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c, mneg));
+                    l_part += p[i];
+                }
+                TL::pv(smem, p, oacc, hb, l32, g);
+            }
+        }
+    }
+
+    if (!wave_active) return;
+    const float l_tot = l_part + __shfl_xor(l_part, 32);
+    if (!my_valid) return;
+    const float inv = 1.0f / l_tot;
+    TL::store_o((T*)a.o + qoff, oacc, inv, g);
+}
+
+template <typename T, int D>
+hipError_t launch(const PrefillArgs& a, hipStream_t st) {
+    const long long nblk = (long long)a.B * a.Hq * a.n_mtiles;
+    hipLaunchKernelGGL((prefill_kernel<T, D>), dim3((unsigned)nblk), dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, hipStream_t st) {
+    if (d == 128) return launch<__bf16, 128>(a, st);
+    if (d == 64) return launch<__bf16, 64>(a, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st) {
+    if (d == 128) return launch<float, 128>(a, st);
+    if (d == 64) return launch<float, 64>(a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace swa

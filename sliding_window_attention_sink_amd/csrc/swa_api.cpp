@@ -1,0 +1,295 @@
+// C ABI of the gfx950 sliding-window attention library (see include/swa.h).
+// Validates every argument on the host before any HIP call, then enqueues the
+// kernels on the caller's stream.  Never allocates, frees or synchronises.
+#include "swa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "swa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int64_t kMaxPos = (int64_t)1 << 30;    // positions and slot counts stay in int32 arithmetic
+
+// Shared descriptor checks; `need_bf16` for entry points built for bf16 only.
+int check_desc(const swa_desc* d, const char* fn) {
+    if (!d) return fail(SWA_ERR_INVALID_ARG, "%s: desc is NULL", fn);
+    if (d->B < 1 || d->Hq < 1 || d->Hkv < 1)
+        return fail(SWA_ERR_INVALID_ARG, "%s: B, Hq, Hkv must be >= 1 (got %d, %d, %d)", fn, d->B, d->Hq, d->Hkv);
+    if (d->Hq % d->Hkv)
+        return fail(SWA_ERR_INVALID_ARG, "%s: Hq (%d) must be a multiple of Hkv (%d)", fn, d->Hq, d->Hkv);
+    if (d->s < 0) return fail(SWA_ERR_INVALID_ARG, "%s: s must be >= 0 (got %d)", fn, d->s);
+    if (d->r < 1) return fail(SWA_ERR_INVALID_ARG, "%s: r must be >= 1 (got %d)", fn, d->r);
+    if ((int64_t)d->s + d->r > kMaxPos)
+        return fail(SWA_ERR_INVALID_ARG, "%s: s + r too large (%lld)", fn, (long long)d->s + d->r);
+    if (!(d->scale > 0.0f) || !std::isfinite(d->scale))
+        return fail(SWA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
+    if (!(d->rope_base >= 0.0f) || !std::isfinite(d->rope_base))
+        return fail(SWA_ERR_INVALID_ARG, "%s: rope_base must be finite and >= 0", fn);
+    if (d->dtype != SWA_F32 && d->dtype != SWA_BF16)
+        return fail(SWA_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, d->dtype);
+    if (d->d != 64 && d->d != 128) return fail(SWA_ERR_UNSUPPORTED, "%s: head dim %d not built (64, 128)", fn, d->d);
+    if (d->rope_base > 0.0f && d->dtype != SWA_BF16)
+        return fail(SWA_ERR_UNSUPPORTED, "%s: RoPE is built for bf16 only", fn);
+    return SWA_OK;
+}
+
+int check_ptr(const void* p, const char* fn, const char* name) {
+    if (!p) return fail(SWA_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+    if (!aligned16(p)) return fail(SWA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);
+    return SWA_OK;
+}
+
+int hip_status(hipError_t e, const char* fn) {
+    if (e == hipSuccess) return SWA_OK;
+    return fail(SWA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+}
+
+size_t elem_bytes(const swa_desc* d) { return d->dtype == SWA_BF16 ? 2 : 4; }
+
+struct RopeLayout {
+    size_t qb, qs, knr, kcr, total;
+};
+
+RopeLayout rope_layout(const swa_desc* d, int64_t L) {
+    RopeLayout r{};
+    const size_t row = (size_t)d->d * 2;
+    const size_t nq = (size_t)d->B * d->Hq * L * row;
+    const size_t nk = (size_t)d->B * d->Hkv * L * row;
+    const size_t nc = (size_t)d->B * d->Hkv * (d->s + d->r) * row;
+    r.qb = 0;
+    r.qs = round_up(r.qb + nq, 256);
+    r.knr = round_up(r.qs + nq, 256);
+    r.kcr = round_up(r.knr + nk, 256);
+    r.total = round_up(r.kcr + nc, 256);
+    return r;
+}
+
+int32_t default_splits(const swa_desc* d) {
+    const int64_t S = (int64_t)d->s + d->r;
+    const int64_t units = (int64_t)d->B * d->Hkv;
+    int64_t n = (2048 + units - 1) / units;
+    int64_t cap = S / 256;
+    if (cap < 1) cap = 1;
+    if (n > cap) n = cap;
+    if (n > 64) n = 64;
+    if (n < 1) n = 1;
+    return (int32_t)n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int swa_abi_version(void) { return SWA_ABI_VERSION; }
+
+const char* swa_last_error(void) { return g_last_error; }
+
+const char* swa_status_str(int status) {
+    switch (status) {
+        case SWA_OK: return "ok";
+        case SWA_ERR_INVALID_ARG: return "invalid argument";
+        case SWA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SWA_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L) {
+    if (check_desc(desc, "swa_prefill_workspace_bytes") != SWA_OK || L < 1) return 0;
+    if (!(desc->rope_base > 0.0f)) return 0;
+    return rope_layout(desc, L).total;
+}
+
+int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
+                const void* k_cache, const void* v_cache, int64_t pos0, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    static const char* fn = "swa_prefill";
+    clear_error();
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k, fn, "k")) || (st = check_ptr(v, fn, "v")) ||
+        (st = check_ptr(o, fn, "o")))
+        return st;
+    if (L < 1) return fail(SWA_ERR_INVALID_ARG, "%s: L must be >= 1 (got %lld)", fn, (long long)L);
+    if (pos0 < 0) return fail(SWA_ERR_INVALID_ARG, "%s: pos0 must be >= 0", fn);
+    if (pos0 + L > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
+    const bool has_cache = k_cache || v_cache;
+    if (has_cache) {
+        if ((st = check_ptr(k_cache, fn, "k_cache")) || (st = check_ptr(v_cache, fn, "v_cache"))) return st;
+    } else if (pos0 != 0) {
+        return fail(SWA_ERR_INVALID_ARG, "%s: pos0 > 0 needs the rolling cache", fn);
+    }
+    const bool rope = desc->rope_base > 0.0f;
+    RopeLayout rl{};
+    if (rope) {
+        rl = rope_layout(desc, L);
+        if ((st = check_ptr(workspace, fn, "workspace"))) return st;
+        if (workspace_bytes < rl.total)
+            return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, rl.total);
+    }
+    const int64_t mtiles = (L + swa::kPrefillRowsPerBlock - 1) / swa::kPrefillRowsPerBlock;
+    if ((int64_t)desc->B * desc->Hq * mtiles > 0x7fffffffLL)
+        return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    swa::PrefillArgs a{};
+    a.q = q;
+    a.qs = q;
+    a.kn = k;
+    a.vn = v;
+    a.kc = has_cache ? k_cache : nullptr;
+    a.vc = has_cache ? v_cache : nullptr;
+    a.o = o;
+    a.L = L;
+    a.pos0 = pos0;
+    a.B = desc->B;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.s = desc->s;
+    a.r = desc->r;
+    a.n_mtiles = (int32_t)mtiles;
+    a.merge_sink = 1;
+    a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
+
+    if (rope) {
+        char* ws = static_cast<char*>(workspace);
+        swa::RopeArgs ra{};
+        ra.q = q;
+        ra.kn = k;
+        ra.kc = has_cache ? k_cache : nullptr;
+        ra.qb = ws + rl.qb;
+        ra.qsk = ws + rl.qs;
+        ra.knr = ws + rl.knr;
+        ra.kcr = ws + rl.kcr;
+        ra.L = L;
+        ra.pos0 = pos0;
+        ra.B = desc->B;
+        ra.Hq = desc->Hq;
+        ra.Hkv = desc->Hkv;
+        ra.s = desc->s;
+        ra.r = desc->r;
+        ra.base = desc->rope_base;
+        if ((st = hip_status(swa::launch_rope_prepare_bf16(ra, desc->d, hs), fn))) return st;
+        a.q = ra.qb;
+        a.qs = ra.qsk;
+        a.kn = ra.knr;
+        a.kc = has_cache ? ra.kcr : nullptr;
+        a.merge_sink = 0;
+    }
+    hipError_t e = desc->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, desc->d, hs)
+                                           : swa::launch_prefill_f32(a, desc->d, hs);
+    return hip_status(e, fn);
+}
+
+int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new, int64_t n, int64_t pos0,
+                     void* k_cache, void* v_cache, void* stream) {
+    static const char* fn = "swa_cache_append";
+    clear_error();
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    if ((st = check_ptr(k_new, fn, "k_new")) || (st = check_ptr(v_new, fn, "v_new")) ||
+        (st = check_ptr(k_cache, fn, "k_cache")) || (st = check_ptr(v_cache, fn, "v_cache")))
+        return st;
+    if (n < 1) return fail(SWA_ERR_INVALID_ARG, "%s: n must be >= 1 (got %lld)", fn, (long long)n);
+    if (pos0 < 0) return fail(SWA_ERR_INVALID_ARG, "%s: pos0 must be >= 0", fn);
+    if (pos0 + n > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
+    swa::AppendArgs a{};
+    a.kn = k_new;
+    a.vn = v_new;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.n = n;
+    a.pos0 = pos0;
+    int64_t first = pos0 + n - desc->r;      // recent tokens before this one are overwritten within the call
+    if (first < pos0) first = pos0;
+    if (first < desc->s) first = desc->s;
+    if (first > pos0 + n) first = pos0 + n;
+    a.first = first;
+    a.B = desc->B;
+    a.Hkv = desc->Hkv;
+    a.s = desc->s;
+    a.r = desc->r;
+    a.d = desc->d;
+    a.elem_bytes = (int32_t)elem_bytes(desc);
+    return hip_status(swa::launch_append(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t swa_decode_default_splits(const swa_desc* desc) {
+    if (check_desc(desc, "swa_decode_default_splits") != SWA_OK) return 0;
+    return default_splits(desc);
+}
+
+size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split) {
+    if (check_desc(desc, "swa_decode_workspace_bytes") != SWA_OK) return 0;
+    if (n_split == 0) n_split = default_splits(desc);
+    if (n_split < 1 || n_split > 64) return 0;
+    return (size_t)desc->B * desc->Hq * n_split * (desc->d + 2) * sizeof(float);
+}
+
+int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const void* v_cache, int64_t T, void* o,
+               int32_t n_split, void* workspace, size_t workspace_bytes, void* stream) {
+    static const char* fn = "swa_decode";
+    clear_error();
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    if (desc->dtype != SWA_BF16) return fail(SWA_ERR_UNSUPPORTED, "%s: decode is built for bf16 only", fn);
+    if (desc->rope_base > 0.0f) return fail(SWA_ERR_UNSUPPORTED, "%s: decode with RoPE is not built", fn);
+    if (desc->Hq / desc->Hkv > 16)
+        return fail(SWA_ERR_UNSUPPORTED, "%s: more than 16 q-heads per kv-head", fn);
+    if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k_cache, fn, "k_cache")) ||
+        (st = check_ptr(v_cache, fn, "v_cache")) || (st = check_ptr(o, fn, "o")) ||
+        (st = check_ptr(workspace, fn, "workspace")))
+        return st;
+    if (T < 1) return fail(SWA_ERR_INVALID_ARG, "%s: T must be >= 1", fn);
+    if (T > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: T beyond 2^30", fn);
+    if (n_split == 0) n_split = default_splits(desc);
+    if (n_split < 1 || n_split > 64) return fail(SWA_ERR_INVALID_ARG, "%s: n_split %d outside 1..64", fn, n_split);
+    const size_t need = (size_t)desc->B * desc->Hq * n_split * (desc->d + 2) * sizeof(float);
+    if (workspace_bytes < need)
+        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if ((int64_t)desc->B * desc->Hkv * n_split > 0x7fffffffLL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
+
+    const int S = desc->s + desc->r;
+    int sps = (S + n_split - 1) / n_split;
+    sps = (sps + 31) / 32 * 32;
+    swa::DecodeArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.o = o;
+    a.ws = static_cast<float*>(workspace);
+    a.T = T;
+    a.B = desc->B;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.s = desc->s;
+    a.r = desc->r;
+    a.n_split = n_split;
+    a.slots_per_split = sps;
+    a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
+    return hip_status(swa::launch_decode_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

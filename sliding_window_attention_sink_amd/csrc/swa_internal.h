@@ -1,0 +1,79 @@
+// Private declarations shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+// Query rows per prefill workgroup (4 waves x 32 rows).
+constexpr int kPrefillRowsPerBlock = 128;
+
+// Plain-old-data arguments of the prefill kernel.  Positions: query row i of
+// the call is token pos0 + i.  Key position p lives at
+//   kc/vc + slot(p) * d   if p < pos0   (rolling cache: slot p if p < s, else s + p mod r)
+//   kn/vn + (p - pos0) * d otherwise (the call's own tokens)
+// per (b, kv-head); q/o per (b, q-head) hold L rows.
+struct PrefillArgs {
+    const void* q;      // band queries (rotated to t when RoPE)
+    const void* qs;     // sink queries (rotated to min(t, s+r-1) when RoPE; == q otherwise)
+    const void* kn;
+    const void* vn;
+    const void* kc;
+    const void* vc;
+    void* o;
+    int64_t L;
+    int64_t pos0;
+    int32_t B, Hq, Hkv, s, r;
+    int32_t n_mtiles;   // query tiles per (b, q-head)
+    int32_t merge_sink; // 1: sinks may share tiles with the band (same queries for both)
+    float scale_log2e;  // scale * log2(e)
+};
+
+struct AppendArgs {
+    const void* kn;     // [B, Hkv, n, d]
+    const void* vn;
+    void* kc;           // [B, Hkv, s + r, d]
+    void* vc;
+    int64_t n;
+    int64_t pos0;
+    int64_t first;      // first token of the call that survives (tokens before it are superseded)
+    int32_t B, Hkv, s, r, d;
+    int32_t elem_bytes;
+};
+
+struct DecodeArgs {
+    const void* q;      // [B, Hq, d]
+    const void* kc;     // [B, Hkv, s + r, d]
+    const void* vc;
+    void* o;            // [B, Hq, d]
+    float* ws;          // [B, Hq, n_split, d + 2]: m (log2 units), l, o[d]
+    int64_t T;          // tokens in the cache including the current one
+    int32_t B, Hq, Hkv, s, r;
+    int32_t n_split;
+    int32_t slots_per_split;
+    float scale_log2e;
+};
+
+struct RopeArgs {
+    const void* q;      // [B, Hq, L, d] chunk queries (pre-rotation)
+    const void* kn;     // [B, Hkv, L, d] chunk keys (pre-rotation)
+    const void* kc;     // [B, Hkv, s + r, d] cache keys (pre-rotation) or null
+    void* qb;           // out: queries rotated to t
+    void* qsk;          // out: queries rotated to min(t, s + r - 1)
+    void* knr;          // out: chunk keys rotated to their position
+    void* kcr;          // out: cache keys rotated to their token's position (valid slots)
+    int64_t L;
+    int64_t pos0;
+    int32_t B, Hq, Hkv, s, r;
+    float base;
+};
+
+// Launchers (return hipError_t of the launch).  `d` selects the instantiation.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, hipStream_t st);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t st);
+hipError_t launch_rope_prepare_bf16(const RopeArgs& a, int d, hipStream_t st);
+
+}  // namespace swa

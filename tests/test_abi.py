@@ -1,0 +1,137 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/swa.h declares, and rejects bad arguments on the host (status code
+and message) before touching the GPU.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_attention_sink_amd import _lib
+from sliding_window_attention_sink_amd._lib import SwaDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+# distinct, 16-byte aligned fake device addresses: validation never dereferences them
+A, B_, C, D, E, F, W = (0x10000 * (i + 1) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(swa_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def desc(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, d=128, s=4, r=28, dtype=_lib.SWA_BF16, scale=0.125, rope_base=0.0)
+    base.update(kw)
+    return SwaDesc(**base)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_match_header(lib):
+    decl = declared_functions()
+    assert decl == sorted(_lib.EXPORTS)
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert lib.swa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert _lib.swa_status_str(0) == "ok"
+    assert _lib.swa_status_str(-1) == "invalid argument"
+    assert _lib.swa_status_str(-2) == "unsupported configuration"
+    assert _lib.swa_status_str(-3) == "HIP error"
+
+
+def prefill(d_, q=A, k=B_, v=C, o=D, L=100, kc=None, vc=None, pos0=0, ws=None, wsb=0):
+    return _lib.swa_prefill(d_, q, k, v, o, L, kc, vc, pos0, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(B=0), -1, "B, Hq, Hkv"),
+    (dict(Hq=6, Hkv=4), -1, "multiple of Hkv"),
+    (dict(s=-1), -1, "s must be"),
+    (dict(r=0), -1, "r must be"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=float("nan")), -1, "scale"),
+    (dict(rope_base=-1.0), -1, "rope_base"),
+    (dict(d=96), -2, "head dim"),
+    (dict(dtype=5), -2, "dtype"),
+    (dict(dtype=_lib.SWA_F32, rope_base=10000.0), -2, "RoPE"),
+])
+def test_prefill_rejects_desc(kw, status, msg):
+    assert prefill(desc(**kw)) == status
+    assert msg in _lib.swa_last_error()
+
+
+def test_prefill_rejects_args(lib):
+    d_ = desc()
+    assert prefill(d_, q=None) == -1 and "q is NULL" in _lib.swa_last_error()
+    assert prefill(d_, o=D + 8) == -1 and "aligned" in _lib.swa_last_error()
+    assert prefill(d_, L=0) == -1 and "L must be" in _lib.swa_last_error()
+    assert prefill(d_, pos0=-1) == -1
+    assert prefill(d_, pos0=5) == -1 and "cache" in _lib.swa_last_error()
+    assert prefill(d_, kc=E, vc=None) == -1 and "v_cache is NULL" in _lib.swa_last_error()
+    assert prefill(d_, L=(1 << 30) + 1) == -1 and "2^30" in _lib.swa_last_error()
+    assert lib.swa_prefill(None, A, B_, C, D, 10, None, None, 0, None, 0, None) == -1
+    assert "desc is NULL" in _lib.swa_last_error()
+
+
+def test_prefill_rope_workspace():
+    d_ = desc(rope_base=10000.0)
+    need = _lib.swa_prefill_workspace_bytes(d_, 100)
+    row = 128 * 2
+    assert need >= (2 * 1 * 4 * 100 + 1 * 2 * (4 + 28 + 100)) * row
+    assert prefill(d_, ws=None) == -1 and "workspace is NULL" in _lib.swa_last_error()
+    assert prefill(d_, ws=W, wsb=need - 1) == -1 and "needed" in _lib.swa_last_error()
+    assert _lib.swa_prefill_workspace_bytes(desc(), 100) == 0
+    assert _lib.swa_prefill_workspace_bytes(desc(r=0), 100) == 0
+
+
+def test_append_rejects():
+    d_ = desc()
+    assert _lib.swa_cache_append(d_, A, B_, 0, 0, C, D, None) == -1 and "n must be" in _lib.swa_last_error()
+    assert _lib.swa_cache_append(d_, A, B_, 4, -2, C, D, None) == -1
+    assert _lib.swa_cache_append(d_, A, None, 4, 0, C, D, None) == -1 and "v_new" in _lib.swa_last_error()
+    assert _lib.swa_cache_append(d_, A, B_, 4, 0, C + 4, D, None) == -1 and "aligned" in _lib.swa_last_error()
+    assert _lib.swa_cache_append(desc(d=80), A, B_, 4, 0, C, D, None) == -2
+
+
+def test_decode_rejects():
+    d_ = desc()
+    ws = _lib.swa_decode_workspace_bytes(d_, 3)
+    assert ws == 1 * 4 * 3 * (128 + 2) * 4
+    dflt = _lib.swa_decode_default_splits(d_)
+    assert 1 <= dflt <= 64
+    assert _lib.swa_decode_workspace_bytes(d_, 0) == 1 * 4 * dflt * 130 * 4
+    assert _lib.swa_decode_workspace_bytes(d_, 65) == 0
+
+    def dec(dd=d_, T=10, n_split=3, wsb=ws, q=A):
+        return _lib.swa_decode(dd, q, B_, C, T, D, n_split, W, wsb, None)
+
+    assert dec(T=0) == -1 and "T must be" in _lib.swa_last_error()
+    assert dec(n_split=65) == -1 and "n_split" in _lib.swa_last_error()
+    assert dec(wsb=ws - 4) == -1 and "workspace" in _lib.swa_last_error()
+    assert dec(q=None) == -1
+    assert dec(dd=desc(dtype=_lib.SWA_F32)) == -2
+    assert dec(dd=desc(rope_base=1e4)) == -2
+    assert dec(dd=desc(Hq=34, Hkv=2)) == -2 and "16 q-heads" in _lib.swa_last_error()
+
+
+def test_last_error_is_per_call():
+    assert prefill(desc(r=0)) == -1
+    assert _lib.swa_last_error() != ""
+    # a later rejected call replaces the message
+    assert prefill(desc(s=-3)) == -1
+    assert "s must be" in _lib.swa_last_error()
+
+
+def test_ctypes_desc_layout():
+    assert ctypes.sizeof(SwaDesc) == 9 * 4
+    assert SwaDesc.scale.offset == 28 and SwaDesc.rope_base.offset == 32

@@ -1,0 +1,142 @@
+"""Rolling-cache append and split-K decode on the GPU against the oracle's
+token-by-token cache simulator (bit-exact slots) and its fp64 decode row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swa_inputs as si
+from gpu_common import TOL, bits, dev, host, max_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def sim_bits(sim):
+    """The simulator's cache as bf16 bit patterns; never-written slots NaN."""
+    return si.bf16_bits(sim.k), si.bf16_bits(sim.v)
+
+
+def assert_cache_equal(kc, vc, sim):
+    kb, vb = sim_bits(sim)
+    written = sim.pos >= 0
+    gk, gv = bits(kc).astype(np.uint16), bits(vc).astype(np.uint16)
+    assert np.array_equal(gk[:, :, written], kb[:, :, written])
+    assert np.array_equal(gv[:, :, written], vb[:, :, written])
+    # never-written slots keep the caller's poison (NaN)
+    idle = torch.from_numpy(np.nonzero(~written)[0]).to(kc.device)
+    assert torch.isnan(kc[:, :, idle].float()).all() and torch.isnan(vc[:, :, idle].float()).all()
+
+
+@pytest.mark.parametrize("s,r,pos0,n", [
+    (4, 60, 0, 3), (4, 60, 0, 64), (4, 60, 0, 200), (4, 60, 2, 5), (4, 60, 70, 1), (4, 60, 61, 130),
+    (0, 32, 0, 100), (3, 5, 0, 17), (70, 30, 0, 75), (70, 30, 50, 40),
+])
+def test_append_bit_exact(gpu, s, r, pos0, n):
+    import sliding_window_attention_sink_amd as swa
+    B, Hkv, d = 2, 3, 128
+    g = np.random.default_rng(s * 1000 + r * 10 + n)
+    hist_k = si.round_bf16(g.standard_normal((B, Hkv, pos0 + n, d)).astype(np.float32))
+    hist_v = si.round_bf16(g.standard_normal((B, Hkv, pos0 + n, d)).astype(np.float32))
+    kc, vc = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    sim = oracle.RollingCacheSim(B, Hkv, d, s, r)
+    say("append", s, r, pos0, n)
+    if pos0:
+        swa.cache_append(dev(hist_k[:, :, :pos0], "bf16"), dev(hist_v[:, :, :pos0], "bf16"), kc, vc, 0, s, r)
+        sim.append(hist_k[:, :, :pos0], hist_v[:, :, :pos0], 0)
+    swa.cache_append(dev(hist_k[:, :, pos0:], "bf16"), dev(hist_v[:, :, pos0:], "bf16"), kc, vc, pos0, s, r)
+    sim.append(hist_k[:, :, pos0:], hist_v[:, :, pos0:], pos0)
+    torch.cuda.synchronize()
+    assert_cache_equal(kc, vc, sim)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,s,r,n_split", [
+    (2, 8, 2, 128, 4, 60, 0),
+    (2, 8, 2, 128, 4, 60, 3),
+    (1, 4, 4, 64, 4, 60, 2),
+    (1, 16, 2, 128, 0, 96, 0),
+    (1, 2, 1, 128, 70, 30, 1),
+])
+def test_decode_steps_match_oracle(gpu, B, Hq, Hkv, d, s, r, n_split):
+    """Append one token, then decode with it, for T = 1 .. 2(s+r)+20: empty
+    slots (poisoned with NaN), the filling cache and the wrapped buffer."""
+    import sliding_window_attention_sink_amd as swa
+    steps = 2 * (s + r) + 20
+    g = np.random.default_rng(B * 100 + Hq + d + s + r)
+    K = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    V = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    Q = si.round_bf16(g.standard_normal((B, Hq, steps, d)).astype(np.float32))
+    kc, vc = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    Kd, Vd, Qd = dev(K, "bf16"), dev(V, "bf16"), dev(Q, "bf16")
+    outs = torch.empty((steps, B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    say("decode steps", B, Hq, Hkv, d, s, r, n_split)
+    for t in range(steps):
+        swa.cache_append(Kd[:, :, t:t + 1].contiguous(), Vd[:, :, t:t + 1].contiguous(), kc, vc, t, s, r)
+        swa.decode(Qd[:, :, t].contiguous(), kc, vc, t + 1, s, r, n_split=n_split, out=outs[t])
+    torch.cuda.synchronize()
+    got = host(outs)
+    rows = np.array([[b, h, t] for t in range(steps) for b in range(B) for h in range(Hq)])
+    ref = oracle.prefill_rows(Q, K, V, s, r, rows=rows).reshape(steps, B, Hq, d)
+    err = max_err(got, ref)
+    assert err <= TOL["bf16"], f"max-abs error {err}"
+
+
+def test_decode_split_counts_agree(gpu):
+    import sliding_window_attention_sink_amd as swa
+    B, Hq, Hkv, d, s, r, T = 2, 8, 2, 128, 4, 1020, 3000
+    g = np.random.default_rng(5)
+    K = si.round_bf16(g.standard_normal((B, Hkv, T, d)).astype(np.float32))
+    V = si.round_bf16(g.standard_normal((B, Hkv, T, d)).astype(np.float32))
+    q = si.round_bf16(g.standard_normal((B, Hq, d)).astype(np.float32))
+    kc, vc = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    say("decode split counts")
+    swa.cache_append(dev(K, "bf16"), dev(V, "bf16"), kc, vc, 0, s, r)
+    qd = dev(q, "bf16")
+    sim = oracle.RollingCacheSim(B, Hkv, d, s, r)
+    sim.append(K, V, 0)
+    ref = np.stack([[oracle.decode_row(sim, q[b, h], b, h, Hq) for h in range(Hq)] for b in range(B)])
+    for ns in (1, 2, 4, 5, 16, 33, 64):
+        o = host(swa.decode(qd, kc, vc, T, s, r, n_split=ns))
+        assert max_err(o, ref) <= TOL["bf16"], ns
+
+
+def test_workload4_full(gpu):
+    """Workload 4 at full size: 8192-token pre-fill in one append call (most of
+    it superseded), cache bit-exact; 1024 decode steps, sampled steps checked
+    against the oracle."""
+    import sliding_window_attention_sink_amd as swa
+    w = si.WORKLOADS[4]
+    hk, hv = si.decode_history(w)
+    say("workload 4 pre-fill")
+    kc, vc = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda", fill=float("nan"))
+    hkd, hvd = dev(hk, "bf16"), dev(hv, "bf16")
+    swa.cache_append(hkd, hvd, kc, vc, 0, w.s, w.r)
+    torch.cuda.synchronize()
+    del hkd, hvd
+    sim = oracle.RollingCacheSim(w.B, w.Hkv, w.d, w.s, w.r)
+    sim.append(hk, hv, 0)
+    assert_cache_equal(kc, vc, sim)
+    del hk, hv
+
+    qs, ks, vs = si.decode_steps(w)
+    qd, kd, vd = dev(qs, "bf16"), dev(ks, "bf16"), dev(vs, "bf16")
+    outs = torch.empty((w.steps, w.B, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+    say("workload 4 steps")
+    for i in range(w.steps):
+        T = w.L + i + 1
+        swa.cache_append(kd[i].unsqueeze(2), vd[i].unsqueeze(2), kc, vc, T - 1, w.s, w.r)
+        swa.decode(qd[i], kc, vc, T, w.s, w.r, out=outs[i])
+    torch.cuda.synchronize()
+    check = {0: 64, 1: 64, 511: 64, 1023: None}
+    g = np.random.default_rng(4)
+    for i in range(w.steps):
+        sim.append(ks[i][:, :, None], vs[i][:, :, None], w.L + i)
+        if i in check:
+            n = check[i]
+            pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+            if n is not None:
+                pairs = [pairs[j] for j in g.choice(len(pairs), n, replace=False)]
+            got = host(outs[i])
+            ref = np.stack([oracle.decode_row(sim, qs[i, b, h], b, h, w.Hq) for b, h in pairs])
+            err = max_err(np.stack([got[b, h] for b, h in pairs]), ref)
+            assert err <= TOL["bf16"], (i, err)
+    assert_cache_equal(kc, vc, sim)

@@ -1,0 +1,167 @@
+"""Prefill on the GPU (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import swa_inputs as si
+from gpu_common import TOL, all_rows, bits, dev, host, max_err, rows_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(q, k, v, s, r, dtype, **kw):
+    import sliding_window_attention_sink_amd as swa
+    o = swa.prefill(dev(q, dtype), dev(k, dtype), dev(v, dtype), s, r, **kw)
+    torch.cuda.synchronize()
+    return o
+
+
+def case_inputs(case_id, B, Hq, Hkv, L, d, dtype, scale=1.0):
+    wid = 1000 + case_id
+    q = si.draw(wid, si.TENSOR_Q, B, Hq, L, d, scale=scale, dtype=dtype)
+    k = si.draw(wid, si.TENSOR_K, B, Hkv, L, d, scale=scale, dtype=dtype)
+    v = si.draw(wid, si.TENSOR_V, B, Hkv, L, d, scale=scale, dtype=dtype)
+    return q, k, v
+
+
+# (case, dtype, B, Hq, Hkv, d, L, s, r): several tiles, ragged tails, GQA,
+# sinks beyond one tile, the r = 1 and r >= L limits, L < s.
+CASES = [
+    (1, "f32", 2, 4, 2, 64, 333, 4, 28),
+    (2, "f32", 1, 2, 2, 128, 200, 0, 1),
+    (3, "f32", 1, 2, 1, 128, 300, 70, 40),
+    (4, "f32", 1, 1, 1, 64, 100, 0, 500),
+    (5, "f32", 1, 3, 3, 64, 5, 4, 2),
+    (6, "bf16", 1, 4, 2, 128, 1000, 4, 300),
+    (7, "bf16", 2, 2, 2, 64, 700, 4, 100),
+    (8, "bf16", 1, 4, 4, 128, 600, 0, 4096),
+    (9, "bf16", 1, 2, 2, 128, 300, 0, 1),
+    (10, "bf16", 1, 2, 2, 128, 520, 70, 130),
+    (11, "bf16", 1, 2, 2, 128, 7, 4, 2),
+    (12, "bf16", 1, 8, 1, 128, 389, 1, 64),
+    (13, "bf16", 1, 2, 2, 128, 1, 4, 28),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{c[0]}_{c[1]}_L{c[6]}_s{c[7]}_r{c[8]}" for c in CASES])
+def test_prefill_matches_oracle(gpu, case):
+    cid, dtype, B, Hq, Hkv, d, L, s, r = case
+    q, k, v = case_inputs(cid, B, Hq, Hkv, L, d, dtype)
+    say("prefill case", case)
+    o = host(run_prefill(q, k, v, s, r, dtype))
+    ref = oracle.prefill_rows(q, k, v, s, r).reshape(B, Hq, L, d)
+    err = max_err(o, ref)
+    assert err <= TOL[dtype], f"max-abs error {err}"
+    if r == 1 and s == 0:
+        # O_t = V_t exactly: one weight of 1
+        grp = Hq // Hkv
+        assert np.array_equal(o, np.repeat(v, grp, axis=1).astype(np.float64))
+
+
+def test_workload1_all_rows(gpu):
+    w = si.WORKLOADS[1]
+    q, k, v = si.prefill_inputs(w)
+    say("workload 1", w.name)
+    o = host(run_prefill(q, k, v, w.s, w.r, w.dtype))
+    ref = oracle.prefill_rows(q, k, v, w.s, w.r).reshape(o.shape)
+    assert max_err(o, ref) <= TOL["f32"]
+
+
+def sample_rows(B, H, L, n, seed, edge=130):
+    g = np.random.default_rng(seed)
+    rows = [np.stack([g.integers(0, B, n), g.integers(0, H, n), g.integers(0, L, n)], axis=1)]
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        ii = np.concatenate([np.arange(0, min(edge, L)), np.arange(max(0, L - edge), L)])
+        rows.append(np.stack([np.full(ii.size, b), np.full(ii.size, h), ii], axis=1))
+    return np.unique(np.concatenate(rows), axis=0)
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_full_workload_sampled_rows(gpu, wid):
+    """Full-size workloads 2 and 3, in the launch configuration the benchmark
+    times, checked on sampled rows (every head touched at random rows, plus
+    the first and last query tiles of two heads)."""
+    w = si.WORKLOADS[wid]
+    q, k, v = si.prefill_inputs(w)
+    say("workload", wid, w.name)
+    o_dev = run_prefill(q, k, v, w.s, w.r, w.dtype)
+    rows = sample_rows(w.B, w.Hq, w.L, 3000, wid)
+    got = host(o_dev[rows[:, 0], rows[:, 1], rows[:, 2]])
+    ref = oracle.prefill_rows(q, k, v, w.s, w.r, rows=rows)
+    err = max_err(got, ref)
+    assert err <= TOL["bf16"], f"max-abs error {err}"
+
+
+def test_uniform_probe_gives_window_mean(gpu):
+    """Q = 0: every weight is equal, O_t = mean of V over U(t) (closed form)."""
+    B, H, L, d, s, r = 1, 2, 777, 128, 4, 50
+    _, k, v = case_inputs(40, B, H, H, L, d, "bf16")
+    q = np.zeros_like(k)
+    say("uniform probe")
+    o = host(run_prefill(q, k, v, s, r, "bf16"))
+    for t in range(L):
+        idx = np.union1d(np.arange(min(s, t + 1)), np.arange(max(0, t - r + 1), t + 1))
+        want = v[:, :, idx].astype(np.float64).mean(axis=2)
+        assert np.abs(o[:, :, t] - want).max() <= 1e-2, t
+
+
+def test_constant_values(gpu):
+    B, H, L, d = 1, 2, 300, 128
+    q, k, _ = case_inputs(41, B, H, H, L, d, "bf16", scale=3.0)
+    v = np.full_like(k, 1.5)
+    say("constant values")
+    o = host(run_prefill(q, k, v, 4, 60, "bf16"))
+    assert np.abs(o - 1.5).max() <= 2.0 ** -8
+
+
+def test_large_sink_scores(gpu):
+    """Sink scores near 100 (beyond fp32 exp's range without max subtraction)
+    that dominate the softmax mass: tests the running-max numerics."""
+    B, H, L, d, s, r = 1, 2, 640, 128, 4, 100
+    g = np.random.default_rng(7)
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    # q = N(0,1) + 3u and sink keys c*u: sink scores c*(3 + N(0,1))/sqrt(d), about 100
+    q = si.round_bf16((g.standard_normal((B, H, L, d)) + 3.0 * u).astype(np.float32))
+    k = si.round_bf16(g.standard_normal((B, H, L, d)).astype(np.float32))
+    v = si.round_bf16(g.standard_normal((B, H, L, d)).astype(np.float32))
+    k[:, :, :s] = si.round_bf16((u * (100.0 * np.sqrt(d) / 3.0)).astype(np.float32))
+    say("large sink scores")
+    o = host(run_prefill(q, k, v, s, r, "bf16"))
+    ref = oracle.prefill_rows(q, k, v, s, r).reshape(o.shape)
+    assert max_err(o, ref) <= TOL["bf16"]
+
+
+def test_deterministic_and_guarded(gpu):
+    """Two runs are bit-identical; nothing is written outside the output."""
+    import sliding_window_attention_sink_amd as swa
+    B, Hq, Hkv, L, d = 1, 4, 2, 450, 128
+    q, k, v = case_inputs(42, B, Hq, Hkv, L, d, "bf16")
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    n = B * Hq * L * d
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + n].view(B, Hq, L, d)
+    say("determinism / guard")
+    swa.prefill(qd, kd, vd, 4, 100, out=out)
+    first = out.clone()
+    swa.prefill(qd, kd, vd, 4, 100, out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(first), bits(out))
+    assert (buf[:pad] == 7.0).all() and (buf[pad + n:] == 7.0).all()
+
+
+def test_stream_argument(gpu):
+    """Work goes to the stream that is passed (here a side stream)."""
+    import sliding_window_attention_sink_amd as swa
+    q, k, v = case_inputs(43, 1, 2, 2, 256, 128, "bf16")
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    side = torch.cuda.Stream()
+    say("side stream")
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o = swa.prefill(qd, kd, vd, 4, 60)
+    side.synchronize()
+    ref = oracle.prefill_rows(q, k, v, 4, 60).reshape(o.shape)
+    assert max_err(host(o), ref) <= TOL["bf16"]
