@@ -82,14 +82,15 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     const int64_t T = a.T;
     const bool all_valid = T >= (int64_t)S;
     // slot j holds a token: sinks j < min(s, T); rolling slot s + q holds the
-    // token p >= s with p mod r == q, and while T < s + r there is at most one
-    // wrap, so p is q or q + r
+    // tokens p >= s with p mod r == q, so it has been written once the first
+    // of them, q + r * ceil((s - q) / r) (or q itself when q >= s), is below T
     auto valid = [&](int j) -> bool {
         if (j >= j1) return false;
         if (all_valid) return true;
         if (j < a.s) return j < T;
         const int64_t q = j - a.s;
-        return (q >= a.s && q <= T - 1) || (q + a.r >= a.s && q + a.r <= T - 1);
+        const int64_t first = q >= a.s ? q : q + (int64_t)a.r * ((a.s - q + a.r - 1) / a.r);
+        return first <= T - 1;
     };
 
     // Q^T operand: column col = head kvh*G + col (zero past the group)

@@ -35,6 +35,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NW = 4;            // waves per workgroup
 constexpr int WROWS = 32;        // query rows per wave
@@ -214,8 +215,11 @@ struct Tiles<float, D> {
         for (int ld = 0; ld < LD; ++ld) {
             int idx = ld * NT + tid;
             int key = idx / CH, c = idx % CH;
+            // bit-cast the whole vector: clang mis-lowers a bit-cast of a single
+            // ext-vector element (every element becomes element 0)
+            const f32x4 kv = __builtin_bit_cast(f32x4, R.k[ld]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S.k[key * KS + 4 * c + e] = __builtin_bit_cast(float, R.k[ld][e]);
+            for (int e = 0; e < 4; ++e) S.k[key * KS + 4 * c + e] = kv[e];
             *(u32x4*)&S.v[key * D + 4 * c] = R.v[ld];
         }
     }
@@ -386,10 +390,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
                 {
-                    auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
-                                                               __builtin_bit_cast(uint32_t, mx), false, false);
-                    mx = fmaxf(mx, fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]),
-                                         __builtin_bit_cast(float, (uint32_t)sw[1])));
+                    const uint32_t mb = __builtin_bit_cast(uint32_t, mx);
+                    const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+                    const uint32_t lo = sw[0], hi = sw[1];
+                    mx = fmaxf(mx, fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi)));
                 }
                 const float mxc = mx * c;
                 const bool upd = mxc > m_c + RESCALE_TH;

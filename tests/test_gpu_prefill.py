@@ -54,9 +54,13 @@ def test_prefill_matches_oracle(gpu, case):
     err = max_err(o, ref)
     assert err <= TOL[dtype], f"max-abs error {err}"
     if r == 1 and s == 0:
-        # O_t = V_t exactly: one weight of 1
-        grp = Hq // Hkv
-        assert np.array_equal(o, np.repeat(v, grp, axis=1).astype(np.float64))
+        # O_t = V_t: a single weight of 1.  bf16 output is exact; in fp32 the
+        # folded scale (exp2 of an fma) leaves the weight within an ulp of 1.
+        want = np.repeat(v, Hq // Hkv, axis=1).astype(np.float64)
+        if dtype == "bf16":
+            assert np.array_equal(o, want)
+        else:
+            assert max_err(o, want) <= 1e-6
 
 
 def test_workload1_all_rows(gpu):
@@ -112,7 +116,9 @@ def test_constant_values(gpu):
     v = np.full_like(k, 1.5)
     say("constant values")
     o = host(run_prefill(q, k, v, 4, 60, "bf16"))
-    assert np.abs(o - 1.5).max() <= 2.0 ** -8
+    # the weights sum to one: O = 1.5 up to the bf16 rounding of P inside
+    # P V (relative 2^-9) and of the output, i.e. within one bf16 ulp (2^-7)
+    assert np.abs(o - 1.5).max() <= 2.0 ** -7
 
 
 def test_large_sink_scores(gpu):
