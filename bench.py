@@ -142,7 +142,7 @@ def bench_decode(torch, swa, w, steps=None):
     qo = 2 * w.B * w.Hq * w.d * 2
     app = w.B * w.Hkv * w.d * 2 * 2
     step_bytes = kv + qo + app
-    return {"ms": ms, "decode_ms": timer.mean_ms(), "bytes_per_step": step_bytes,
+    return {"ms": ms, "decode_ms": timer.mean_ms(), "bytes_per_step": step_bytes, "steps": steps,
             "gbs": step_bytes / ms / 1e6, "decode_kernel_bytes": kv + qo}
 
 
@@ -215,7 +215,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time the main workload only")
+    ap.add_argument("--extra", default="3,4,5,1",
+                    help="other workloads to time alongside (comma list of 1,3,4,5 or 'none')")
+    ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's 1024)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -231,34 +236,49 @@ def main():
         sys.exit(1)
     swa.load()
 
+    if args.copy_calibration:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE per dispatch of
+        # this kernel are the counters' reading for 1 GiB read + 1 GiB written
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 2, "dispatches": 3}))
+        return
+
     w = si.WORKLOADS[2]
     log("main workload", w.name)
     main_res = bench_prefill(torch, swa, w, args.steps, args.warmup)
     log("main", main_res)
 
     extra = {}
-    if not args.only_main:
+    todo = set() if (args.only_main or args.extra == "none") else {int(x) for x in args.extra.split(",") if x}
+    if 3 in todo:
         w3 = si.WORKLOADS[3]
         r3 = bench_prefill(torch, swa, w3, max(5, args.steps // 2), 2)
         extra[w3.name] = {"tflops": r3["tflops"], "ms": r3["ms"], "kernel_ms": r3["kernel_ms"],
                           "frac_bf16_peak": r3["tflops"] / PEAK_BF16_TFLOPS}
         log("w3", r3)
         torch.cuda.empty_cache()
+    if 4 in todo:
         w4 = si.WORKLOADS[4]
-        r4 = bench_decode(torch, swa, w4)
+        r4 = bench_decode(torch, swa, w4, args.decode_steps)
         dec_gbs = r4["decode_kernel_bytes"] / r4["decode_ms"] / 1e6
-        extra[w4.name] = {"GB/s": r4["gbs"], "us_per_step": r4["ms"] * 1e3, "steps": w4.steps,
+        extra[w4.name] = {"GB/s": r4["gbs"], "us_per_step": r4["ms"] * 1e3, "steps": r4["steps"],
                           "bytes_per_step": r4["bytes_per_step"], "frac_hbm_peak": r4["gbs"] / PEAK_HBM_GBS,
                           "decode_launch_us": r4["decode_ms"] * 1e3, "decode_launch_GB/s": dec_gbs,
                           "decode_launch_frac_hbm_peak": dec_gbs / PEAK_HBM_GBS}
         log("w4", r4)
         torch.cuda.empty_cache()
+    if 5 in todo:
         w5 = si.WORKLOADS[5]
         r5 = bench_chunked(torch, swa, w5)
         extra[w5.name] = {"tflops": r5["tflops"], "ms": r5["ms"], "frac_bf16_peak": r5["tflops"] / PEAK_BF16_TFLOPS,
                           "prefill_call_ms": r5["prefill_call_ms"]}
         log("w5", r5)
         torch.cuda.empty_cache()
+    if 1 in todo:
         w1 = si.WORKLOADS[1]
         r1 = bench_prefill(torch, swa, w1, 20, 3)
         extra[w1.name] = {"tflops": r1["tflops"], "ms": r1["ms"], "frac_f32_peak": r1["tflops"] / PEAK_F32_TFLOPS}

@@ -100,6 +100,38 @@ struct Tiles<__bf16, D> {
         }
     }
 
+    // Tile rows that are consecutive in memory (the call's own tokens).
+    static __device__ __forceinline__ void load_contig(Regs& R, const __bf16* kb, const __bf16* vb, int tid) {
+        const int kofs = (tid / CH) * D + (tid % CH) * 8;
+#pragma unroll
+        for (int ld = 0; ld < K_LD; ++ld) R.k[ld] = *(const u32x4*)(kb + kofs + ld * (NT / CH) * D);
+        if (tid < V_TASKS) {
+            const int vofs = 4 * (tid / CH) * D + (tid % CH) * 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) R.v[j] = *(const u32x4*)(vb + vofs + j * D);
+        }
+    }
+
+    // Tile rows inside the rolling part of the cache: key k of the tile is
+    // slot slot0 + k, wrapping from s + r back to s.
+    static __device__ __forceinline__ void load_ring(Regs& R, const __bf16* kc, const __bf16* vc, int slot0,
+                                                     int slot_end, int r, int tid) {
+#pragma unroll
+        for (int ld = 0; ld < K_LD; ++ld) {
+            int sl = slot0 + ld * (NT / CH) + tid / CH;
+            sl = sl >= slot_end ? sl - r : sl;
+            R.k[ld] = *(const u32x4*)(kc + (size_t)sl * D + (tid % CH) * 8);
+        }
+        if (tid < V_TASKS) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                int sl = slot0 + 4 * (tid / CH) + j;
+                sl = sl >= slot_end ? sl - r : sl;
+                R.v[j] = *(const u32x4*)(vc + (size_t)sl * D + (tid % CH) * 8);
+            }
+        }
+    }
+
     static __device__ __forceinline__ void store(Smem& S, const Regs& R, int tid) {
 #pragma unroll
         for (int ld = 0; ld < K_LD; ++ld) {
@@ -210,6 +242,26 @@ struct Tiles<float, D> {
         }
     }
 
+    static __device__ __forceinline__ void load_contig(Regs& R, const float* kb, const float* vb, int tid) {
+        const int ofs = (tid / CH) * D + (tid % CH) * 4;
+#pragma unroll
+        for (int ld = 0; ld < LD; ++ld) {
+            R.k[ld] = *(const u32x4*)(kb + ofs + ld * (NT / CH) * D);
+            R.v[ld] = *(const u32x4*)(vb + ofs + ld * (NT / CH) * D);
+        }
+    }
+
+    static __device__ __forceinline__ void load_ring(Regs& R, const float* kc, const float* vc, int slot0,
+                                                     int slot_end, int r, int tid) {
+#pragma unroll
+        for (int ld = 0; ld < LD; ++ld) {
+            int sl = slot0 + ld * (NT / CH) + tid / CH;
+            sl = sl >= slot_end ? sl - r : sl;
+            R.k[ld] = *(const u32x4*)(kc + (size_t)sl * D + (tid % CH) * 4);
+            R.v[ld] = *(const u32x4*)(vc + (size_t)sl * D + (tid % CH) * 4);
+        }
+    }
+
     static __device__ __forceinline__ void store(Smem& S, const Regs& R, int tid) {
 #pragma unroll
         for (int ld = 0; ld < LD; ++ld) {
@@ -283,7 +335,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
     const int s = a.s, r = a.r;
     const int pos0 = (int)a.pos0;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: keep it scalar
     const int l32 = lane & 31, g = lane >> 5;
 
     const int row0 = mt * BM;                                   // first row of the tile (call-relative)
@@ -359,12 +412,26 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
             q_loaded = want_q;
         }
 
-        TL::load(regs, P.first * BN, tid, kptr, vptr, loadable);
+        // Tile-uniform choice of the load path: rows that every query of the
+        // tile may need, all in the call's own tokens or all in the rolling
+        // part of the cache, take a fast path; edge tiles check every row.
+        auto load_tile = [&](int j) {
+            const int kbase = j * BN, klast = kbase + BN - 1;
+            const bool all_needed = klast <= t1 && (kbase >= lo_any || klast < P.sink_hi);
+            if (all_needed && kbase >= pos0) {
+                TL::load_contig(regs, kn + (size_t)(kbase - pos0) * D, vn + (size_t)(kbase - pos0) * D, tid);
+            } else if (all_needed && kbase >= s && klast < pos0) {
+                TL::load_ring(regs, kc, vc, s + kbase % r, s + r, r, tid);
+            } else {
+                TL::load(regs, kbase, tid, kptr, vptr, loadable);
+            }
+        };
+        load_tile(P.first);
         for (int j = P.first; j <= P.last; ++j) {
             __syncthreads();
             TL::store(smem, regs, tid);
             __syncthreads();
-            if (j < P.last) TL::load(regs, (j + 1) * BN, tid, kptr, vptr, loadable);
+            if (j < P.last) load_tile(j + 1);
             if (!wave_active) continue;
 
             const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
