@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libswa.so")
 
-SOURCES = ["swa_api.cpp", "prefill.hip", "decode.hip", "append.hip", "rope.hip"]
+SOURCES = ["swa_api.cpp", "prefill.hip", "prefill_bf16.hip", "decode.hip", "append.hip", "rope.hip"]
 ARCH = "gfx950"
 
 
@@ -35,6 +35,9 @@ def _flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
             # packed fp32 VALU ops stay off: ordinary float code only
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # the kernels never produce NaN (masked scores are -inf), so max
+            # needs no NaN canonicalisation; infinities keep IEEE semantics
+            "-fno-honor-nans",
             "-Wno-unused-command-line-argument"]
 
 

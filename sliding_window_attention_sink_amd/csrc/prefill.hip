@@ -1,4 +1,6 @@
-// Banded flash-style prefill for sliding-window attention with sinks, gfx950.
+// Banded flash-style prefill for sliding-window attention with sinks, gfx950:
+// the fp32 kernel (bf16 inputs go to the ping-pong kernel in prefill_bf16.hip,
+// which uses the same tiling, masks and accumulator layouts).
 //
 // Row t attends U(t) = {i <= t : i < s or i >= t - r + 1} (sinks plus the r
 // most recent keys, each once; hyper.ai summary of arXiv 2608.28444, section
@@ -14,7 +16,7 @@
 //    merge when they touch, with the single mask "i < s or i >= t - r + 1";
 //  * each wave owns 32 query rows and skips 32-key blocks that are masked for
 //    all of them;
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (fp32: v_mfma_f32_32x32x2_f32):
+//  * S^T = K Q^T on v_mfma_f32_32x32x2_f32:
 //    the accumulator gives every lane one query row (lanes l and l+32 share
 //    it), so the row max needs one cross-lane exchange and the row sum none
 //    until the end;
@@ -23,195 +25,23 @@
 //    keeps O's rescaling rare and the result exact (the same max enters the
 //    numerator and the denominator);
 //  * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
-//    accumulator (rows of K are fed to the MFMA in a permuted order so each
-//    lane's eight P values are eight consecutive keys), V is transposed into
-//    LDS so that those eight keys are one 16-byte read.
-#include "swa_internal.h"
+//    accumulator; with one key per lane per MFMA step, V stays row-major in
+//    LDS.
+#include "prefill_common.h"
 
 namespace swa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace pf;
+
 
 constexpr int NW = 4;            // waves per workgroup
-constexpr int WROWS = 32;        // query rows per wave
 constexpr int BM = NW * WROWS;   // query rows per workgroup
-static_assert(BM == kPrefillRowsPerBlock, "host tiling must match");
-constexpr int BN = 64;           // key positions per LDS tile
+static_assert(BM == kPrefillF32RowsPerBlock, "host tiling must match");
 constexpr int NT = NW * 64;      // threads per workgroup
-constexpr float RESCALE_TH = 8.0f;  // log2 units: raise the running max only past 2^8
-constexpr int NO_BAND = 0x7fffffff;
-
-// MFMA row rho of a 32-key block holds key swap23(rho) (bits 2 and 3 swapped).
-// With that order the 32x32 accumulator element i of lane group g holds key
-// 16*(i/8) + 8*g + (i%8): eight consecutive keys per PV k-step.
-__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
-__device__ __forceinline__ constexpr int keyoff(int i, int g) { return 16 * (i / 8) + 8 * g + (i % 8); }
-
-struct Phase {
-    int first, last;     // tile indices, inclusive
-    int sink_hi;         // keys < sink_hi are sinks
-    int band_lo;         // band keys are >= max(band_lo, t - r + 1)
-    int use_qs;          // read the sink queries
-};
 
 template <typename T, int D>
 struct Tiles;
-
-// ---------------------------------------------------------------- bf16 tiles
-template <int D>
-struct Tiles<__bf16, D> {
-    static constexpr int CH = D / 8;                    // 16-byte chunks per key row
-    static constexpr int K_LD = BN * CH / NT;           // K chunks per thread
-    static constexpr int V_TASKS = (BN / 4) * CH;       // (4 keys x 8 dims) blocks per tile
-    static constexpr int QK_STEPS = D / 16;
-    struct Smem {
-        u32x4 k[BN * CH];          // [key][chunk ^ swz_k(key)]
-        u32x4 vt[D * (BN / 8)];    // [dim][8-key chunk ^ swz_v(dim)]
-    };
-    struct Regs { u32x4 k[K_LD]; u32x4 v[4]; };
-    typedef bf16x8 QReg;
-    static constexpr int QREGS = QK_STEPS;
-
-    static __device__ __forceinline__ int swz_k(int key) { return swap23(key & 15) & (CH - 1); }
-    static __device__ __forceinline__ int swz_v(int dim) { return (dim ^ (dim >> 3)) & 7; }
-
-    template <class KPtr, class VPtr, class Loadable>
-    static __device__ __forceinline__ void load(Regs& R, int kbase, int tid, KPtr kptr, VPtr vptr,
-                                                Loadable ok) {
-#pragma unroll
-        for (int ld = 0; ld < K_LD; ++ld) {
-            int idx = ld * NT + tid;
-            int key = idx / CH, c = idx % CH;
-            int p = kbase + key;
-            R.k[ld] = ok(p) ? *(const u32x4*)(kptr(p) + c * 8) : u32x4{0, 0, 0, 0};
-        }
-        if (tid < V_TASKS) {
-            int kq = tid / CH, dc = tid % CH;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int p = kbase + 4 * kq + j;
-                R.v[j] = ok(p) ? *(const u32x4*)(vptr(p) + dc * 8) : u32x4{0, 0, 0, 0};
-            }
-        }
-    }
-
-    // Tile rows that are consecutive in memory (the call's own tokens).
-    static __device__ __forceinline__ void load_contig(Regs& R, const __bf16* kb, const __bf16* vb, int tid) {
-        const int kofs = (tid / CH) * D + (tid % CH) * 8;
-#pragma unroll
-        for (int ld = 0; ld < K_LD; ++ld) R.k[ld] = *(const u32x4*)(kb + kofs + ld * (NT / CH) * D);
-        if (tid < V_TASKS) {
-            const int vofs = 4 * (tid / CH) * D + (tid % CH) * 8;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) R.v[j] = *(const u32x4*)(vb + vofs + j * D);
-        }
-    }
-
-    // Tile rows inside the rolling part of the cache: key k of the tile is
-    // slot slot0 + k, wrapping from s + r back to s.
-    static __device__ __forceinline__ void load_ring(Regs& R, const __bf16* kc, const __bf16* vc, int slot0,
-                                                     int slot_end, int r, int tid) {
-#pragma unroll
-        for (int ld = 0; ld < K_LD; ++ld) {
-            int sl = slot0 + ld * (NT / CH) + tid / CH;
-            sl = sl >= slot_end ? sl - r : sl;
-            R.k[ld] = *(const u32x4*)(kc + (size_t)sl * D + (tid % CH) * 8);
-        }
-        if (tid < V_TASKS) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int sl = slot0 + 4 * (tid / CH) + j;
-                sl = sl >= slot_end ? sl - r : sl;
-                R.v[j] = *(const u32x4*)(vc + (size_t)sl * D + (tid % CH) * 8);
-            }
-        }
-    }
-
-    static __device__ __forceinline__ void store(Smem& S, const Regs& R, int tid) {
-#pragma unroll
-        for (int ld = 0; ld < K_LD; ++ld) {
-            int idx = ld * NT + tid;
-            int key = idx / CH, c = idx % CH;
-            S.k[key * CH + (c ^ swz_k(key))] = R.k[ld];
-        }
-        if (tid < V_TASKS) {
-            int kq = tid / CH, dc = tid % CH;
-            // 4 keys x 8 dims -> 8 dims x 4 keys
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                const int w = e >> 1;
-                u32x2 cell;
-                cell[0] = __builtin_amdgcn_perm(R.v[1][w], R.v[0][w], sel);
-                cell[1] = __builtin_amdgcn_perm(R.v[3][w], R.v[2][w], sel);
-                int dim = dc * 8 + e;
-                int chunk = (kq >> 1) ^ swz_v(dim);
-                ((u32x2*)S.vt)[(dim * (BN / 8) + chunk) * 2 + (kq & 1)] = cell;
-            }
-        }
-    }
-
-    static __device__ __forceinline__ void load_q(QReg* q, const __bf16* row, bool valid, int g) {
-#pragma unroll
-        for (int ks = 0; ks < QK_STEPS; ++ks) {
-            u32x4 x = valid ? *(const u32x4*)(row + 16 * ks + 8 * g) : u32x4{0, 0, 0, 0};
-            q[ks] = __builtin_bit_cast(bf16x8, x);
-        }
-    }
-
-    // S^T block (32 keys x 32 rows) of half-block hb.
-    static __device__ __forceinline__ f32x16 qk(const Smem& S, const QReg* q, int hb, int l32, int g) {
-        f32x16 acc = {};
-        const int key = hb * 32 + swap23(l32);
-        const int sw = swz_k(key);
-#pragma unroll
-        for (int ks = 0; ks < QK_STEPS; ++ks) {
-            bf16x8 a = __builtin_bit_cast(bf16x8, S.k[key * CH + ((2 * ks + g) ^ sw)]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], acc, 0, 0, 0);
-        }
-        return acc;
-    }
-
-    // O^T += V^T P^T for half-block hb; p holds exp'd scores in accumulator order.
-    static __device__ __forceinline__ void pv(const Smem& S, const float* p, f32x16* o, int hb, int l32, int g) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 b;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = (__bf16)p[8 * kk + e];
-            const int c16 = 4 * hb + 2 * kk + g;   // 16-byte chunk of 8 keys in a V^T row
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int dim = 32 * db + l32;
-                const int chunk = c16 ^ swz_v(dim);
-                const u32x4 x = S.vt[dim * (BN / 8) + chunk];
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), b, o[db], 0, 0, 0);
-            }
-        }
-    }
-
-    static __device__ __forceinline__ void store_o(__bf16* row, const f32x16* o, float inv, int g) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                __bf16 v0 = (__bf16)(o[db][4 * q4 + 0] * inv);
-                __bf16 v1 = (__bf16)(o[db][4 * q4 + 1] * inv);
-                __bf16 v2 = (__bf16)(o[db][4 * q4 + 2] * inv);
-                __bf16 v3 = (__bf16)(o[db][4 * q4 + 3] * inv);
-                u32x2 w;
-                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-                *(u32x2*)(row + 32 * db + 8 * q4 + 4 * g) = w;
-            }
-        }
-    }
-};
 
 // ---------------------------------------------------------------- fp32 tiles
 template <int D>
@@ -313,15 +143,6 @@ struct Tiles<float, D> {
     }
 };
 
-// Maps blockIdx to a work item so that each XCD (blocks are dealt to the 8
-// XCDs round-robin) gets one contiguous run of work items: neighbouring query
-// tiles of a head, which read overlapping key tiles, then share that XCD's L2.
-__device__ __forceinline__ int xcd_work_item(int bid, int nblk) {
-    const int x = bid & 7, k = bid >> 3;
-    const int per = nblk >> 3, rem = nblk & 7;
-    return x * per + (x < rem ? x : rem) + k;
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
     typedef Tiles<T, D> TL;
@@ -367,27 +188,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
 
     // ---- phases (uniform over the workgroup)
     Phase ph0 = {0, -1, 0, NO_BAND, 0}, ph1 = {0, -1, 0, NO_BAND, 0};
-    int nph = 0;
-    {
-        const int sink_end = s < t1 + 1 ? s : t1 + 1;           // keys [0, sink_end) are sinks
-        const int band_lo = s > t0 - r + 1 ? s : t0 - r + 1;    // lowest band key of the tile
-        const bool has_sink = sink_end > 0, has_band = band_lo <= t1;
-        const int st_last = has_sink ? (sink_end - 1) / BN : -1;
-        const int bt_first = band_lo / BN, bt_last = t1 / BN;
-        const Phase sink_ph = {0, st_last, s, NO_BAND, 1};
-        const Phase band_ph = {bt_first, bt_last, 0, s, 0};
-        if (a.merge_sink && has_sink && has_band && bt_first <= st_last + 1) {
-            ph0 = Phase{0, bt_last, s, s, 0};
-            nph = 1;
-        } else if (has_sink) {
-            ph0 = sink_ph;
-            ph1 = band_ph;
-            nph = has_band ? 2 : 1;
-        } else if (has_band) {
-            ph0 = band_ph;
-            nph = 1;
-        }
-    }
+    const int nph = make_phases(t0, t1, s, r, a.merge_sink != 0, ph0, ph1);
 
     typename TL::QReg qreg[TL::QREGS];
     f32x16 oacc[D / 32];
@@ -456,12 +257,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
                 float mx = sacc[0];
 #pragma unroll
                 for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-                {
-                    const uint32_t mb = __builtin_bit_cast(uint32_t, mx);
-                    const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
-                    const uint32_t lo = sw[0], hi = sw[1];
-                    mx = fmaxf(mx, fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi)));
-                }
+                mx = max_pair_lanes(mx);
                 const float mxc = mx * c;
                 const bool upd = mxc > m_c + RESCALE_TH;
                 if (__builtin_amdgcn_ballot_w64(upd)) {
@@ -500,12 +296,6 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
 }
 
 }  // namespace
-
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, hipStream_t st) {
-    if (d == 128) return launch<__bf16, 128>(a, st);
-    if (d == 64) return launch<__bf16, 64>(a, st);
-    return hipErrorInvalidValue;
-}
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st) {
     if (d == 128) return launch<float, 128>(a, st);

@@ -149,7 +149,10 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
         if (workspace_bytes < rl.total)
             return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, rl.total);
     }
-    const int64_t mtiles = (L + swa::kPrefillRowsPerBlock - 1) / swa::kPrefillRowsPerBlock;
+    const bool bf16 = desc->dtype == SWA_BF16;
+    const int64_t rows_per_block =
+        bf16 ? swa::prefill_bf16_rows_per_block(desc->Hq, desc->Hkv) : swa::kPrefillF32RowsPerBlock;
+    const int64_t mtiles = (L + rows_per_block - 1) / rows_per_block;
     if ((int64_t)desc->B * desc->Hq * mtiles > 0x7fffffffLL)
         return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
 
@@ -171,6 +174,7 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
     a.r = desc->r;
     a.n_mtiles = (int32_t)mtiles;
     a.merge_sink = 1;
+    a.pair_mode = (bf16 && (desc->Hq / desc->Hkv) % 2 == 0) ? 1 : 0;
     a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
 
     if (rope) {
@@ -198,8 +202,7 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
         a.kc = has_cache ? ra.kcr : nullptr;
         a.merge_sink = 0;
     }
-    hipError_t e = desc->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, desc->d, hs)
-                                           : swa::launch_prefill_f32(a, desc->d, hs);
+    hipError_t e = bf16 ? swa::launch_prefill_bf16(a, desc->d, hs) : swa::launch_prefill_f32(a, desc->d, hs);
     return hip_status(e, fn);
 }
 

@@ -6,8 +6,8 @@
 
 namespace swa {
 
-// Query rows per prefill workgroup (4 waves x 32 rows).
-constexpr int kPrefillRowsPerBlock = 128;
+// Query rows per workgroup of the fp32 prefill kernel (4 waves x 32 rows).
+constexpr int kPrefillF32RowsPerBlock = 128;
 
 // Plain-old-data arguments of the prefill kernel.  Positions: query row i of
 // the call is token pos0 + i.  Key position p lives at
@@ -27,6 +27,7 @@ struct PrefillArgs {
     int32_t B, Hq, Hkv, s, r;
     int32_t n_mtiles;   // query tiles per (b, q-head)
     int32_t merge_sink; // 1: sinks may share tiles with the band (same queries for both)
+    int32_t pair_mode;  // bf16 kernel: workgroup = two q-heads of one kv-head (else 256 rows of one head)
     float scale_log2e;  // scale * log2(e)
 };
 
@@ -68,6 +69,9 @@ struct RopeArgs {
     int32_t B, Hq, Hkv, s, r;
     float base;
 };
+
+// Query rows per workgroup of the bf16 prefill kernel for this head layout.
+int prefill_bf16_rows_per_block(int Hq, int Hkv);
 
 // Launchers (return hipError_t of the launch).  `d` selects the instantiation.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, hipStream_t st);
