@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -33,6 +34,36 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+MAIN_KERNEL = "prefill_pp_kernel<128>"
+# HBM bytes per launch of MAIN_KERNEL on the main workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE runs scaled by a plain-copy calibration; valid only
+# while the kernel sources hash to the value recorded beside it.
+TRAFFIC_NOTE = os.path.join(ROOT, "profiles", "prefill_pp_kernel_gqa32x8_L8192_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "sliding_window_attention_sink_amd", "csrc", f)
+                  for f in ("prefill_bf16.hip", "prefill_common.h", "swa_internal.h")]
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per launch from the counter note, or None if absent or stale."""
+    try:
+        text = open(TRAFFIC_NOTE).read()
+    except OSError:
+        return None
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)\s*$", text, re.M)
+    m_h = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != kernel_sources_sha256():
+        return None
+    return int(m_b.group(1))
 
 
 def log(*a):
@@ -299,9 +330,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L, "s": w.s, "r": w.r,
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<bf16,128>", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": MAIN_KERNEL, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": recorded_traffic()},
         "extra": extra,
     }
     if not args.no_cpu_baseline:
