@@ -1,4 +1,4 @@
-// Banded flash-style prefill, bf16 inputs, gfx950: the ping-pong kernel.
+// Banded flash-style prefill, bf16 inputs, gfx950.
 //
 // Row t attends U(t) = {i <= t : i < s or i >= t - r + 1} (sinks plus the r
 // most recent keys, each once; hyper.ai summary of arXiv 2608.28444, section
@@ -13,24 +13,25 @@
 //     kv-head over the same 128 tokens;
 //   * otherwise: the groups take the two 128-row halves of 256 tokens of one
 //     q-head.
-// Each wave owns 32 query rows.  Per 64-key tile a wave does two phases:
-//   M: S^T = K Q^T for the tile's two 32-key halves (two independent chains
-//      of v_mfma_f32_32x32x16_bf16, 16 MFMAs);
-//   S: online softmax of those scores in fp32 (VALU) and O^T += V^T P^T
-//      (16 MFMAs).
-// Group 1 runs one phase behind group 0 and a workgroup barrier closes every
-// phase, so on each SIMD one wave issues QK MFMAs while the other runs the
-// softmax and its PV MFMAs: the matrix unit stays busy while the vector unit
-// works.  Key tiles are double-buffered in LDS and fetched two phases ahead.
+// Each wave owns 32 query rows and alternates two clusters per 64-key tile:
+//   C(v): MFMA only: O^T += V^T P^T for tile v-1 and S^T = K Q^T for tile v
+//         (32 v_mfma_f32_32x32x16_bf16 in six independent chains, operands
+//         read from LDS a few steps ahead);
+//   X(v): VALU only: the online softmax of tile v's scores into bf16 P, and
+//         the direct global->LDS loads of a later tile.
+// Group 1 runs one cluster behind group 0 and a workgroup barrier closes each
+// cluster, so on every SIMD one wave streams MFMAs while the other does the
+// exponentials: a wave never waits for the matrix unit with vector work
+// queued behind its MFMAs.  K and V tiles rotate through three LDS buffer
+// sets and are fetched four clusters before use.
 //
-// Layout details (see the fp32 kernel in prefill.hip for the same scheme):
-// the 32x32 S^T accumulator gives every lane one query row (lanes l and l+32
+// The 32x32 S^T accumulator gives every lane one query row (lanes l and l+32
 // share it), so the row max is one v_permlane32_swap exchange; K rows enter
 // the MFMA in a permuted order so that each lane's eight P values are eight
-// consecutive keys; V is stored transposed in LDS so those eight keys of one
-// dimension are a single 16-byte read.  The running max is raised only when a
-// tile's max exceeds it by more than 2^8 (exact: the same max scales the
-// numerator and the denominator).
+// consecutive keys, which makes the accumulator itself the P^T operand.  V
+// stays row-major in LDS and ds_read_b64_tr_b16 delivers it transposed.  The
+// running max is raised only when a tile's max exceeds it by more than 2^8
+// (exact: the same max scales the numerator and the denominator).
 #include "prefill_common.h"
 
 namespace swa {
@@ -39,131 +40,164 @@ namespace {
 using namespace pf;
 
 constexpr int PW = 8;             // waves per workgroup
+constexpr int GW = 4;             // waves per group
 constexpr int PNT = PW * 64;      // threads per workgroup
+constexpr int NSET = 3;           // LDS buffer sets
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D>
 struct PP {
     static constexpr int CH = D / 8;                 // 16-byte chunks per key row
-    static constexpr int KCH = CH + 1;               // padded K row (chunks)
-    static constexpr int VCH = BN / 8 + 1;           // padded V^T row (chunks of 8 keys)
-    static constexpr int K_LD = BN * CH / PNT;       // K chunks per thread per tile
-    static constexpr int V_TASKS = (BN / 4) * CH;    // blocks of 4 keys x 8 dims per tile
-    static constexpr int QK_STEPS = D / 16;
-    static_assert(K_LD >= 1 && V_TASKS <= 256, "tile shape");
+    static constexpr int RPB = 64 / CH;              // key rows per 1 KB block: 4 or 8
+    static constexpr int NINS = BN * CH / 64;        // direct-load instructions per K (or V) tile
+    static constexpr int JN = NINS / GW;             // ... per wave of the loading group
+    static constexpr int JSTEP = RPB * GW;           // key rows between a wave's successive instructions
+    static constexpr int RB = D * 2;                 // bytes per key row
+    static constexpr int QK_STEPS = D / 16;          // k-steps of S^T = K Q^T; also rounds of a cluster
+    static constexpr int NDB = D / 32;               // 32-dim blocks of O^T
+    static_assert(NINS % GW == 0 && 2 * QK_STEPS == 4 * NDB, "tile shape");
 
-    // Padded rows keep every operand address affine in the loop indices (one
-    // base register per lane plus immediate offsets) and the reads free of
-    // bank conflicts: 8 or 16 lanes reading consecutive rows at one column hit
-    // distinct banks.
+    // K tile: LDS row rho holds key krow(rho) (MFMA row order: key
+    // 32h + swap23(x) at row 32h + x), in 1 KB blocks of RPB rows stored
+    // chunk-major with a block-dependent swizzle:
+    //   chunk c of row rho at  (rho / RPB) KB + (c ^ ksw(rho / RPB)) * 16 RPB + (rho % RPB) * 16,
+    // so the MFMA operand reads (16 lanes, 16 consecutive rows, one chunk)
+    // cover 16 distinct bank groups.  V tile: rows = keys in order, chunk c
+    // of row k at chunk c ^ vsw(k), so the transposing reads (4 rows x 64
+    // bytes per 32 lanes) are free of bank conflicts.  Both tiles are written
+    // by direct global->LDS loads, one instruction per 1 KB block.
     struct Buf {
-        u32x4 k[BN * KCH];         // row = MFMA row order: key 32h + swap23(x) at row 32h + x
-        u32x4 vt[D * VCH];         // row = dim, chunk = 8 keys
-    };
-    struct Regs {
-        u32x4 k[K_LD];
-        u32x4 v[4];
+        u32x4 k[BN * CH];
+        u32x4 v[BN * CH];
     };
 
     static __device__ __forceinline__ int krow(int key) { return (key & ~31) | swap23(key & 31); }
-    // V work is spread over waves 0, 1, 4, 5; consecutive lanes take
-    // consecutive 4-key groups so the transposed 8-byte writes of 16 lanes
-    // cover all banks once.
-    static __device__ __forceinline__ int vtask(int tid) { return (tid & 127) | ((tid >> 8) << 7); }
-    static __device__ __forceinline__ bool has_v(int tid) {
-        return ((tid >> 7) & 1) == 0 && vtask(tid) < V_TASKS;
+    static __device__ __forceinline__ int ksw(int blk) { return D == 128 ? (blk & 3) : (blk & 1); }
+    static __device__ __forceinline__ int vsw(int k) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+
+    // Direct-load maps for wave `sub` of the loading group: its instruction
+    // j fills block i = sub + GW j.  The lane's key row is key0 + JSTEP j and
+    // its byte offset inside the row is chk (both independent of j).
+    //   K: lane l -> block position l = (chunk l / RPB, row l % RPB).
+    //   V: lane l -> row RPB i + l / CH, physical chunk l % CH.
+    static __device__ __forceinline__ void k_map(int sub, int lane, int& key0, int& chk) {
+        key0 = krow(RPB * sub + lane % RPB);
+        chk = ((lane / RPB) ^ ksw(sub)) * 16;
     }
-    static __device__ __forceinline__ int v_kq(int vt) { return vt & 15; }
-    static __device__ __forceinline__ int v_dc(int vt) { return vt >> 4; }
-
-    // Per-thread rows of a tile: K chunk ld is row k_row(ld, tid), chunk tid % CH;
-    // V rows 4 kq + j (j < 4), chunk dc (threads with has_v only).
-    static __device__ __forceinline__ int k_row(int ld, int tid) { return ld * (PNT / CH) + tid / CH; }
-    static __device__ __forceinline__ int v_row(int j, int tid) { return 4 * v_kq(vtask(tid)) + j; }
-
-    // One set of loads from per-row pointers (all load paths share it).
-    static __device__ __forceinline__ void load_rows(Regs& R, const __bf16* const* kp, const __bf16* const* vp,
-                                                     int tid) {
-#pragma unroll
-        for (int ld = 0; ld < K_LD; ++ld) R.k[ld] = *(const u32x4*)(kp[ld] + (tid % CH) * 8);
-        if (has_v(tid)) {
-            const int dc = v_dc(vtask(tid));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) R.v[j] = *(const u32x4*)(vp[j] + dc * 8);
-        }
+    static __device__ __forceinline__ void v_map(int sub, int lane, int& key0, int& chk) {
+        key0 = RPB * sub + lane / CH;
+        chk = ((lane % CH) ^ vsw(lane / CH)) * 16;
     }
 
-    static __device__ __forceinline__ void store(Buf& S, const Regs& R, int tid) {
-#pragma unroll
-        for (int ld = 0; ld < K_LD; ++ld) {
-            const int idx = ld * PNT + tid;
-            const int key = idx / CH, c = idx % CH;
-            S.k[krow(key) * KCH + c] = R.k[ld];
-        }
-        if (has_v(tid)) {
-            const int vt = vtask(tid), kq = v_kq(vt), dc = v_dc(vt);
-            // 4 keys x 8 dims -> 8 dims x 4 keys (8-byte cells)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                const int w = e >> 1;
-                u32x2 cell;
-                cell[0] = __builtin_amdgcn_perm(R.v[1][w], R.v[0][w], sel);
-                cell[1] = __builtin_amdgcn_perm(R.v[3][w], R.v[2][w], sel);
-                const int dim = dc * 8 + e;
-                ((u32x2*)S.vt)[(dim * VCH + (kq >> 1)) * 2 + (kq & 1)] = cell;
-            }
+    // Per-lane byte offsets of the K operand reads: step ks of half hb reads
+    // k_rd(ks) + hb * 32 rows.  D = 128: the swizzle flips chunk bits 0-1, so
+    // even and odd steps use two bases; D = 64: one base.
+    static __device__ __forceinline__ void k_rd_bases(int l32, int g, int& be, int& bo) {
+        const int blk = l32 / RPB, x = ksw(blk);
+        const int common = blk * 1024 + (l32 % RPB) * 16;
+        if (D == 128) {
+            be = common + (g ^ (x & 1)) * 64 + (x >> 1) * 128;
+            bo = common + (g ^ (x & 1)) * 64 + ((x >> 1) ^ 1) * 128;
+        } else {
+            be = bo = common + (g ^ x) * 128;
         }
     }
+    static constexpr int k_rd_step(int ks) { return D == 128 ? (ks >> 1) * 256 : ks * 256; }
+    static constexpr int K_HALF = 32 * RB;           // bytes between the two 32-row halves (32 rows = 32 / RPB blocks)
 
-    // A wave's 32 query rows in LDS (padded rows like K): row l32 holds the
-    // query of lane l32, read as the B operand of S^T = K Q^T.
-    struct QTile {
-        u32x4 q[WROWS * KCH];
+    // A wave's 32 query rows in registers, as the B operand of S^T = K Q^T:
+    // lane (l32, g) holds row l32, chunks 2 ks + g for ks < D/16.
+    struct QRegs {
+        u32x4 q[QK_STEPS];
     };
 
-    // Fill the wave's Q tile: lane l copies row l % 32, half g of its chunks.
-    static __device__ __forceinline__ void load_q(QTile& Q, const __bf16* row, bool valid, int l32, int g) {
+    static __device__ __forceinline__ void load_q(QRegs& Q, const __bf16* row, bool valid, int g) {
 #pragma unroll
-        for (int j = 0; j < CH / 2; ++j) {
-            const int c = 2 * j + g;
-            Q.q[l32 * KCH + c] = valid ? *(const u32x4*)(row + 8 * c) : u32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < QK_STEPS; ++ks)
+            Q.q[ks] = valid ? *(const u32x4*)(row + 8 * (2 * ks + g)) : u32x4{0, 0, 0, 0};
+    }
+
+    // Byte offset in a V tile of this lane's transposing reads for d-block db.
+    // ds_read_b64_tr_b16 hands lane 16q + 4a + j element e of the four
+    // 16-bit values lane 16q + a + 4e reads, so lane 16q + a + 4e reads key
+    // 8 (q/2) + e (plus the k-step's base) at dims 16 (q&1) + 4a .. +3 of the
+    // block, and every lane receives V[key][dim l%32] for four keys.
+    static __device__ __forceinline__ int v_base(int lane, int db) {
+        const int a = lane & 3, e = (lane >> 2) & 3, q = lane >> 4;
+        const int row = 8 * (q >> 1) + e;
+        const int chunk = (4 * db + 2 * (q & 1) + (a >> 1)) ^ vsw(e);
+        return row * RB + chunk * 16 + 8 * (a & 1);
+    }
+
+    // The V^T operand of PV product n of a cluster: half hb = n / (2 NDB),
+    // k-step kk = (n / NDB) % 2, d-block db = n % NDB (two transposing reads:
+    // keys 8 g' + 0..3 and + 4..7 of the k-step).
+    static __device__ __forceinline__ bf16x8 v_op(const Buf& S, const int* vb, int n) {
+        const int hb = n / (2 * NDB), kk = (n / NDB) % 2, db = n % NDB;
+        const char* p = (const char*)S.v + vb[db] + (32 * hb + 16 * kk) * RB;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * RB));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+
+    // The MFMA cluster C: QK_STEPS rounds, each with one step of both S^T
+    // chains (K of tile v, Q; starting from 0) and two PV products of tile
+    // v-1 (V, P in pk: half hb, k-step kk at pk[2 hb + kk]).  Operands are
+    // read LA rounds ahead; mid() runs once, after the first round's MFMAs
+    // are issued.
+    template <bool QK, bool PV, class Mid>
+    static __device__ __forceinline__ void cluster(const Buf& S, const QRegs& Q, const int* vb, const bf16x8* pk,
+                                                   int kbe, int kbo, f32x16& a0, f32x16& a1, f32x16* o, Mid&& mid) {
+        constexpr int LA = 2;
+        constexpr int R = QK_STEPS;
+        const char* kbase = (const char*)S.k;
+        u32x4 ka[LA + 1], kb[LA + 1];
+        bf16x8 va[LA + 1][2];
+        auto rd = [&](int i) {
+            const int sl = i % (LA + 1);
+            if (QK) {
+                const char* p = kbase + ((i & 1) ? kbo : kbe) + k_rd_step(i);
+                ka[sl] = *(const u32x4*)p;
+                kb[sl] = *(const u32x4*)(p + K_HALF);
+            }
+            if (PV) {
+                va[sl][0] = v_op(S, vb, 2 * i);
+                va[sl][1] = v_op(S, vb, 2 * i + 1);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < LA; ++i) rd(i);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            if (i + LA < R) rd(i + LA);
+            const int sl = i % (LA + 1);
+            const bf16x8 q = __builtin_bit_cast(bf16x8, Q.q[i]);
+            if (QK) a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[sl]), q,
+                                                                 i == 0 ? f32x16{} : a0, 0, 0, 0);
+            if (PV) {
+                const int n = 2 * i;
+                o[n % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[sl][0], pk[n / NDB], o[n % NDB], 0, 0, 0);
+            }
+            if (QK) a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kb[sl]), q,
+                                                                 i == 0 ? f32x16{} : a1, 0, 0, 0);
+            if (PV) {
+                const int n = 2 * i + 1;
+                o[n % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[sl][1], pk[n / NDB], o[n % NDB], 0, 0, 0);
+            }
+            if (i == 0) mid();
+            // keep each round's reads ahead of the MFMAs that follow (the
+            // scheduler would otherwise sink them next to their uses)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // S^T for both 32-key halves as two independent MFMA chains, accumulated
-    // onto the seeds already in a0, a1 (0, or -inf on masked elements).
-    static __device__ __forceinline__ void qk2(const Buf& S, const QTile& Q, int l32, int g, f32x16& a0, f32x16& a1) {
-        const u32x4* k0 = &S.k[l32 * KCH + g];
-        const u32x4* k1 = k0 + 32 * KCH;
-        const u32x4* qq = &Q.q[l32 * KCH + g];
-#pragma unroll
-        for (int ks = 0; ks < QK_STEPS; ++ks) {
-            const bf16x8 q = __builtin_bit_cast(bf16x8, qq[2 * ks]);
-            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0[2 * ks]), q, a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1[2 * ks]), q, a1, 0, 0, 0);
-        }
-    }
-
-    // Same with zero-initialised accumulators (the first MFMA takes C = 0).
-    static __device__ __forceinline__ void qk2_zero(const Buf& S, const QTile& Q, int l32, int g, f32x16& a0,
-                                                    f32x16& a1) {
-        const u32x4* k0 = &S.k[l32 * KCH + g];
-        const u32x4* k1 = k0 + 32 * KCH;
-        const u32x4* qq = &Q.q[l32 * KCH + g];
-        const bf16x8 q0 = __builtin_bit_cast(bf16x8, qq[0]);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0[0]), q0, f32x16{}, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1[0]), q0, f32x16{}, 0, 0, 0);
-#pragma unroll
-        for (int ks = 1; ks < QK_STEPS; ++ks) {
-            const bf16x8 q = __builtin_bit_cast(bf16x8, qq[2 * ks]);
-            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0[2 * ks]), q, a0, 0, 0, 0);
-            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1[2 * ks]), q, a1, 0, 0, 0);
-        }
-    }
-
-    // P of half hb as two bf16x8 operands (accumulator order): exp2 of the
-    // scaled, max-shifted scores, packed pairwise as they are produced; the
-    // fp32 values only feed this lane's share of the row sum.
+    // P of one half as two bf16x8 operands (accumulator order): exp2 of the
+    // scaled, max-shifted scores, packed pairwise; the fp32 values feed this
+    // lane's share of the row sum (plain adds: the packed dot-product
+    // instructions share the matrix pipe and would stall beside the MFMAs of
+    // the other wave).
     static __device__ __forceinline__ void softmax_pack(const f32x16& sc, float c, float mneg, float& l,
                                                         bf16x8& b0, bf16x8& b1) {
 #pragma unroll
@@ -181,24 +215,20 @@ struct PP {
         }
     }
 
-    // O^T += V^T P^T for half hb.
-    static __device__ __forceinline__ void pv(const Buf& S, const bf16x8& b0, const bf16x8& b1, f32x16* o, int hb,
-                                              int l32, int g) {
-        const u32x4* v = &S.vt[l32 * VCH + g];
+    // Row max over both halves (v_max3 tree).
+    static __device__ __forceinline__ float max2x16(const f32x16& x, const f32x16& y) {
+        float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 b = kk ? b1 : b0;
+        for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, x[i]), x[i + 1]);
+        m = fmaxf(fmaxf(m, x[15]), y[0]);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const u32x4 x = v[db * 32 * VCH + 4 * hb + 2 * kk];
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), b, o[db], 0, 0, 0);
-            }
-        }
+        for (int i = 1; i < 15; i += 2) m = fmaxf(fmaxf(m, y[i]), y[i + 1]);
+        return fmaxf(m, y[15]);
     }
 
     static __device__ __forceinline__ void store_o(__bf16* row, const f32x16* o, float inv, int g) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int db = 0; db < NDB; ++db) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const uint32_t v0 = __builtin_bit_cast(uint16_t, (__bf16)(o[db][4 * q4 + 0] * inv));
@@ -214,11 +244,45 @@ struct PP {
     }
 };
 
+// One 16-byte direct global->LDS load per lane: lane l's chunk lands at
+// lds + 16 l (lds is wave-uniform).  Written as inline asm so that the
+// compiler, which cannot tell which LDS bytes the load writes, does not make
+// every later LDS read wait for it; the kernel waits for these loads itself
+// (wait_vm) before the barrier that publishes the tile.
+__device__ __forceinline__ void load_lds16(const void* gp, void* lds) {
+    const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(la) : "m0");
+}
+
+// Same from a wave-uniform base plus a per-lane unsigned byte offset.
+__device__ __forceinline__ void load_lds16_off(const void* base, uint32_t off, void* lds) {
+    const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(la) : "m0");
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding.
+__device__ __forceinline__ void wait_vm(int n) {
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+}
+
+// Workgroup barrier without a memory fence (the direct loads are waited
+// for explicitly); the empty asm statements keep the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     typedef PP<D> T;
-    __shared__ typename T::Buf smem[2];
-    __shared__ typename T::QTile qsm[PW];
+    __shared__ typename T::Buf smem[NSET];
 
     const int s = a.s, r = a.r;
     const int pos0 = (int)a.pos0;
@@ -263,16 +327,6 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     const __bf16* vn = (const __bf16*)a.vn + (size_t)(b * a.Hkv + kvh) * a.L * D;
     const __bf16* kc = a.kc ? (const __bf16*)a.kc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
     const __bf16* vc = a.vc ? (const __bf16*)a.vc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
-    auto kptr = [&](int p) -> const __bf16* {
-        if (p >= pos0) return kn + (size_t)(p - pos0) * D;
-        const int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
-        return kc + (size_t)sl * D;
-    };
-    auto vptr = [&](int p) -> const __bf16* {
-        if (p >= pos0) return vn + (size_t)(p - pos0) * D;
-        const int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
-        return vc + (size_t)sl * D;
-    };
 
     // ---- tiles of the workgroup: phase 0 then phase 1, as one list
     Phase ph0 = {0, -1, 0, NO_BAND, 0}, ph1 = {0, -1, 0, NO_BAND, 0};
@@ -283,113 +337,130 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     auto phase_of = [&](int v) -> Phase { return v < n0 ? ph0 : ph1; };
     auto tile_of = [&](int v) -> int { return v < n0 ? ph0.first + v : ph1.first + (v - n0); };
 
-    typename T::Regs regs;
-    // Rows of tile v: rows every query of the workgroup may need, all in the
-    // call's own tokens (contiguous) or all in the rolling part of the cache
-    // (slot slot0 + row with one wrap), take a direct formula; other tiles
-    // clamp each row to one the tile does need.  A clamped row is real,
-    // finite data that the score mask then removes (-inf score, weight 0).
-    auto load_tile = [&](int v) {
+    // ---- direct loads: a tile's K (or V) is brought in by the 4 waves of
+    // one group; wave `sub` issues instructions sub, sub + 4, ...
+    int kkey0, kchk, vkey0, vchk;
+    T::k_map(sub, lane, kkey0, kchk);
+    T::v_map(sub, lane, vkey0, vchk);
+    int kbe, kbo;
+    T::k_rd_bases(l32, g, kbe, kbo);
+
+    // Rows of tile v: when every query of the workgroup may need every row
+    // of the tile and the rows are all in the call's own tokens (contiguous)
+    // or all in the rolling part of the cache (slot s + p mod r, one wrap),
+    // a direct formula; otherwise each row is clamped to one the tile does
+    // need.  A clamped row is real, finite data that the score mask then
+    // removes (-inf score, weight 0).  Returns the number of loads issued.
+    auto issue = [&](int v, bool is_k, int set) -> int {
         const Phase P = phase_of(v);
         const int kbase = tile_of(v) * BN, klast = kbase + BN - 1;
         const int lo_any = P.band_lo > t0 - r + 1 ? P.band_lo : t0 - r + 1;
         const bool all_needed = klast <= t1 && (kbase >= lo_any || klast < P.sink_hi);
-        const __bf16* kp[T::K_LD];
-        const __bf16* vp[4];
+        const __bf16* own = is_k ? kn : vn;
+        const __bf16* cache = is_k ? kc : vc;
+        const int key0 = is_k ? kkey0 : vkey0;
+        const int chk = is_k ? kchk : vchk;
+        u32x4* dst0 = is_k ? smem[set].k : smem[set].v;
         if (all_needed && kbase >= pos0) {
-            const __bf16* kb = kn + (size_t)(kbase - pos0) * D;
-            const __bf16* vb = vn + (size_t)(kbase - pos0) * D;
+            // the call's own rows kbase.. (contiguous)
+            const uint32_t lo = (uint32_t)(key0 * T::RB + chk);
 #pragma unroll
-            for (int ld = 0; ld < T::K_LD; ++ld) kp[ld] = kb + T::k_row(ld, tid) * D;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vp[j] = vb + T::v_row(j, tid) * D;
+            for (int j = 0; j < T::JN; ++j)
+                load_lds16_off(own + (size_t)(kbase - pos0 + T::JSTEP * j) * D, lo, dst0 + 64 * (sub + GW * j));
         } else if (all_needed && kbase >= s && klast < pos0) {
-            const int slot0 = s + kbase % r, slot_end = s + r;
+            // rolling cache slots s + (p mod r), at most one wrap in a tile
+            const __bf16* base = cache + (size_t)s * D;
+            const int rel0 = kbase % r;
 #pragma unroll
-            for (int ld = 0; ld < T::K_LD; ++ld) {
-                int sl = slot0 + T::k_row(ld, tid);
-                sl = sl >= slot_end ? sl - r : sl;
-                kp[ld] = kc + (size_t)sl * D;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                int sl = slot0 + T::v_row(j, tid);
-                sl = sl >= slot_end ? sl - r : sl;
-                vp[j] = vc + (size_t)sl * D;
+            for (int j = 0; j < T::JN; ++j) {
+                int rel = rel0 + key0 + T::JSTEP * j;
+                rel = rel >= r ? rel - r : rel;
+                load_lds16_off(base, (uint32_t)(rel * T::RB + chk), dst0 + 64 * (sub + GW * j));
             }
         } else {
-            // nearest needed row: past t1 -> t1; between the sinks and the
-            // band -> the band's first row, or the last sink if the phase has
-            // no band rows
+            // each row clamped to one the tile needs: past t1 -> t1; between
+            // the sinks and the band -> the band's first row, or the last
+            // sink if the phase has no band rows
             const int gap_to = lo_any <= t1 ? lo_any : P.sink_hi - 1;
-            auto clamp = [&](int p) {
+#pragma unroll
+            for (int j = 0; j < T::JN; ++j) {
+                int p = kbase + key0 + T::JSTEP * j;
                 p = (p >= P.sink_hi && p < lo_any) ? gap_to : p;
-                return p < t1 ? p : t1;
-            };
-#pragma unroll
-            for (int ld = 0; ld < T::K_LD; ++ld) kp[ld] = kptr(clamp(kbase + T::k_row(ld, tid)));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vp[j] = vptr(clamp(kbase + T::v_row(j, tid)));
+                p = p < t1 ? p : t1;
+                const __bf16* rowp;
+                if (p >= pos0) {
+                    rowp = own + (size_t)(p - pos0) * D;
+                } else {
+                    const int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
+                    rowp = cache + (size_t)sl * D;
+                }
+                load_lds16((const char*)rowp + chk, dst0 + 64 * (sub + GW * j));
+            }
         }
-        T::load_rows(regs, kp, vp, tid);
+        return T::JN;
     };
 
     // ---- per-wave state
-    typename T::QTile& qt = qsm[wave];
+    typename T::QRegs qr;
     int q_loaded = -1;
-    f32x16 oacc[D / 32];
+    f32x16 oacc[T::NDB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < T::NDB; ++db) oacc[db] = f32x16{};
+    int vb[T::NDB];
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db) vb[db] = T::v_base(lane, db);
     float m_c = -__builtin_inff();
     float l_part = 0.0f;
     const float c = a.scale_log2e;
-    f32x16 sacc0 = {}, sacc1 = {};     // scores of the tile between its M and S phases
-    bool need0 = false, need1 = false, full0 = false, full1 = false;
+    f32x16 sacc0 = {}, sacc1 = {};     // scores of a tile, from its C to its X cluster
+    bf16x8 pk[4];                      // P of a tile, from its X cluster to the next C
 
-    // M phase: scores of tile v
-    auto phase_m = [&](int v) {
+    // The queries tile v is scored with (RoPE: the sink phase uses queries
+    // rotated to min(t, s+r-1)); reloaded only when the phase changes, and
+    // waited for here so no later instruction waits on it.
+    auto ensure_q = [&](int v) {
+        const int want_q = (phase_of(v).use_qs && a.qs != a.q) ? 1 : 0;
+        if (want_q != q_loaded) {
+            T::load_q(qr, (const __bf16*)(want_q ? a.qs : a.q) + qoff, my_valid, g);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            q_loaded = want_q;
+        }
+    };
+
+    // C(v), 1 <= v < nv: PV of tile v-1 and QK of tile v, both from buffer
+    // set v % 3, with this group's loads for a later tile issued after the
+    // first round.  A tile the wave does not need is still multiplied (its
+    // scores are dropped, its weights are 0), which keeps one code path.
+    // X(v): online softmax of tile v's scores into pk (zeros when no row of
+    // the wave needs the tile); the mask is applied only to tiles that are
+    // not inside every row's key set.
+    auto cluster_x = [&](int v) {
         const Phase P = phase_of(v);
         const int kb = tile_of(v) * BN;
         const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
         const int lo_w1 = P.band_lo > tw1 - r + 1 ? P.band_lo : tw1 - r + 1;
-        need0 = kb <= tw1 && (kb < P.sink_hi || kb + 31 >= lo_w0);
-        need1 = kb + 32 <= tw1 && (kb + 32 < P.sink_hi || kb + 63 >= lo_w0);
-        full0 = kb + 31 <= tw0 && (kb >= lo_w1 || kb + 31 < P.sink_hi);
-        full1 = kb + 63 <= tw0 && (kb + 32 >= lo_w1 || kb + 63 < P.sink_hi);
-        if (!need0 && !need1) return;   // the whole tile is masked for these rows
-        const int want_q = (P.use_qs && a.qs != a.q) ? 1 : 0;
-        if (want_q != q_loaded) {
-            T::load_q(qt, (const __bf16*)(want_q ? a.qs : a.q) + qoff, my_valid, l32, g);
-            q_loaded = want_q;
-        }
-        if (full0 && full1) {
-            T::qk2_zero(smem[v & 1], qt, l32, g, sacc0, sacc1);
+        const bool need = kb <= tw1 && (kb < P.sink_hi || kb + 63 >= lo_w0);
+        if (!need) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
             return;
         }
-        // seed the score accumulators with the mask: 0 where the key is in
-        // U(t), -inf elsewhere (-inf plus any finite product stays -inf).
-        // Element i of half hb is key kb + 32 hb + 8 g + k_i, k_i an immediate;
-        // a half no row of this wave needs comes out all -inf.
-        const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
-        const int kbg = kb + 8 * g;
-        const int lim_t = my_t - kbg, lim_s = P.sink_hi - kbg, lim_b = lo_me - kbg;
+        const bool full = kb + 63 <= tw0 && (kb >= lo_w1 || kb + 63 < P.sink_hi);
         const float NEG = -__builtin_inff();
+        if (!full) {
+            // key kb + 32 hb + 8 g + k_i of element i of half hb (k_i an
+            // immediate) is in U(t) iff k <= t and (k < sink_hi or k >= lo(t))
+            const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
+            const int kbg = kb + 8 * g;
+            const int lim_t = my_t - kbg, lim_s = P.sink_hi - kbg, lim_b = lo_me - kbg;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
-            sacc0[i] = (k0 <= lim_t && (k0 < lim_s || k0 >= lim_b)) ? 0.0f : NEG;
-            sacc1[i] = (k1 <= lim_t && (k1 < lim_s || k1 >= lim_b)) ? 0.0f : NEG;
+            for (int i = 0; i < 16; ++i) {
+                const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
+                sacc0[i] = (k0 <= lim_t && (k0 < lim_s || k0 >= lim_b)) ? sacc0[i] : NEG;
+                sacc1[i] = (k1 <= lim_t && (k1 < lim_s || k1 >= lim_b)) ? sacc1[i] : NEG;
+            }
         }
-        T::qk2(smem[v & 1], qt, l32, g, sacc0, sacc1);
-    };
-
-    // S phase: online softmax of tile v's scores, then O^T += V^T P^T
-    auto phase_s = [&](int v) {
-        if (!need0 && !need1) return;
-        const float NEG = -__builtin_inff();
-        float mx = NEG;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc0[i], sacc1[i]));
+        float mx = T::max2x16(sacc0, sacc1);
         mx = max_pair_lanes(mx);
         const float mxc = mx * c;
         const bool upd = mxc > m_c + RESCALE_TH;
@@ -398,65 +469,100 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
             m_c = upd ? mxc : m_c;
             l_part *= alpha;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         }
         const float mneg = (m_c == NEG) ? 0.0f : -m_c;
-        const typename T::Buf& B = smem[v & 1];
-        {
-            bf16x8 b0, b1;
-            T::softmax_pack(sacc0, c, mneg, l_part, b0, b1);
-            T::pv(B, b0, b1, oacc, 0, l32, g);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        {
-            bf16x8 b0, b1;
-            T::softmax_pack(sacc1, c, mneg, l_part, b0, b1);
-            T::pv(B, b0, b1, oacc, 1, l32, g);
-        }
+        T::softmax_pack(sacc0, c, mneg, l_part, pk[0], pk[1]);
+        T::softmax_pack(sacc1, c, mneg, l_part, pk[2], pk[3]);
     };
 
-    // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight
+    // ---- schedule.  Half-slot hs: group 0 runs C(v) at hs = 2v and X(v) at
+    // 2v+1, group 1 runs X(v-1) at 2v and C(v) at 2v+1; a barrier ends every
+    // half-slot.  C(v) reads K of tile v and V of tile v-1 from set v % 3
+    // during half-slots 2v and 2v+1.  Group 0's C(v) fetches K of tile v+2
+    // and group 1's C(v) fetches V of tile v+1, both into set (v+2) % 3
+    // (last read at 2v-1); a wave ends each half-slot waiting for all but
+    // its latest batch of loads, so every batch lands at least one barrier
+    // before its first reader.  C(0) (no PV) and C(nv) (no QK) are peeled off
+    // the loop.
+    int n_last = 0;
     if (nv > 0) {
-        load_tile(0);
-        T::store(smem[0], regs, tid);
-    }
-    if (nv > 1) {
-        load_tile(1);
-        T::store(smem[1], regs, tid);
-    }
-    if (nv > 2) load_tile(2);
-    __syncthreads();
-
-    // ---- slots: group 0 runs M(v) in slot 2v and S(v) in slot 2v+1; group 1
-    // one slot later.  Tile k is stored in slot 2k-1 (its buffer was last read
-    // by group 1's S(k-2) in slot 2k-2) and fetched from memory in slot 2k-3.
-    // Each group runs its own straight-line loop (same barriers in the same
-    // order), so no value has to be merged between an M and an S path.
-    auto stage = [&](int slot) {
-        if ((slot & 1) && slot >= 3) {
-            const int k = (slot + 1) >> 1;
-            if (k < nv) {
-                T::store(smem[k & 1], regs, tid);
-                if (k + 1 < nv) load_tile(k + 1);
-            }
+        if (grp == 0) {
+            issue(0, true, 0);
+            issue(0, false, 1);
+        } else if (nv > 1) {
+            issue(1, true, 1);
         }
-        __syncthreads();
+    }
+    wait_vm(0);
+    wg_barrier();
+    auto end_half = [&]() {
+        wait_vm(n_last);
+        wg_barrier();
     };
-    if (grp == 0) {
-        for (int v = 0; v <= nv; ++v) {
-            if (wave_active && v < nv) phase_m(v);
-            stage(2 * v);
-            if (wave_active && v < nv) phase_s(v);
-            stage(2 * v + 1);
+    // this group's loads during C(v) into set nset
+    auto c_loads = [&](int v, int nset) {
+        if (grp == 0) n_last = (v + 2 < nv) ? issue(v + 2, true, nset) : 0;
+        else n_last = (v + 1 < nv) ? issue(v + 1, false, nset) : 0;
+    };
+    auto c_first = [&]() {
+        if (wave_active) {
+            ensure_q(0);
+            T::template cluster<true, false>(smem[0], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [&] { c_loads(0, 2); });
+        } else {
+            c_loads(0, 2);
         }
-    } else {
-        for (int v = 0; v <= nv; ++v) {
-            if (wave_active && v >= 1) phase_s(v - 1);
-            stage(2 * v);
-            if (wave_active && v < nv) phase_m(v);
-            stage(2 * v + 1);
+    };
+    auto c_mid = [&](int v, int set, int nset) {
+        if (wave_active) {
+            ensure_q(v);
+            T::template cluster<true, true>(smem[set], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [&] { c_loads(v, nset); });
+        } else {
+            c_loads(v, nset);
+        }
+    };
+    auto c_last = [&](int set) {
+        n_last = 0;
+        if (wave_active)
+            T::template cluster<false, true>(smem[set], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
+    };
+    if (nv > 0) {
+        if (grp == 0) {
+            c_first();
+            end_half();
+            if (wave_active) cluster_x(0);
+            end_half();
+            int set = 1;                       // v % 3
+            for (int v = 1; v < nv; ++v) {
+                const int nset = set == 0 ? 2 : set - 1;   // (v + 2) % 3
+                c_mid(v, set, nset);
+                end_half();
+                if (wave_active) cluster_x(v);
+                end_half();
+                set = set == 2 ? 0 : set + 1;
+            }
+            c_last(set);
+            end_half();
+            end_half();
+        } else {
+            end_half();
+            c_first();
+            end_half();
+            int set = 1;
+            for (int v = 1; v < nv; ++v) {
+                const int nset = set == 0 ? 2 : set - 1;
+                if (wave_active) cluster_x(v - 1);
+                end_half();
+                c_mid(v, set, nset);
+                end_half();
+                set = set == 2 ? 0 : set + 1;
+            }
+            if (wave_active) cluster_x(nv - 1);
+            end_half();
+            c_last(set);
+            end_half();
         }
     }
 
