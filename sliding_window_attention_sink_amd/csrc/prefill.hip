@@ -175,12 +175,12 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
     const T* kc = a.kc ? (const T*)a.kc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
     const T* vc = a.vc ? (const T*)a.vc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
 
-    auto kptr = [&](int p) -> const T* {
+    auto kptr = [&](int p) __attribute__((always_inline)) -> const T* {
         if (p >= pos0) return kn + (size_t)(p - pos0) * D;
         int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
         return kc + (size_t)sl * D;
     };
-    auto vptr = [&](int p) -> const T* {
+    auto vptr = [&](int p) __attribute__((always_inline)) -> const T* {
         if (p >= pos0) return vn + (size_t)(p - pos0) * D;
         int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
         return vc + (size_t)sl * D;
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
         const Phase P = pi ? ph1 : ph0;
         // a key position is loaded iff some row of this tile needs it
         const int lo_any = P.band_lo > t0 - r + 1 ? P.band_lo : t0 - r + 1;
-        auto loadable = [&](int p) { return p <= t1 && (p < P.sink_hi || p >= lo_any); };
+        auto loadable = [&](int p) __attribute__((always_inline)) { return p <= t1 && (p < P.sink_hi || p >= lo_any); };
 
         const int want_q = (P.use_qs && a.qs != a.q) ? 1 : 0;
         if (want_q != q_loaded) {
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
         // Tile-uniform choice of the load path: rows that every query of the
         // tile may need, all in the call's own tokens or all in the rolling
         // part of the cache, take a fast path; edge tiles check every row.
-        auto load_tile = [&](int j) {
+        auto load_tile = [&](int j) __attribute__((always_inline)) {
             const int kbase = j * BN, klast = kbase + BN - 1;
             const bool all_needed = klast <= t1 && (kbase >= lo_any || klast < P.sink_hi);
             if (all_needed && kbase >= pos0) {

@@ -32,6 +32,8 @@
 // stays row-major in LDS and ds_read_b64_tr_b16 delivers it transposed.  The
 // running max is raised only when a tile's max exceeds it by more than 2^8
 // (exact: the same max scales the numerator and the denominator).
+#include <type_traits>
+
 #include "prefill_common.h"
 
 namespace swa {
@@ -155,7 +157,7 @@ struct PP {
         const char* kbase = (const char*)S.k;
         u32x4 ka[LA + 1], kb[LA + 1];
         bf16x8 va[LA + 1][2];
-        auto rd = [&](int i) {
+        auto rd = [&](int i) __attribute__((always_inline)) {
             const int sl = i % (LA + 1);
             if (QK) {
                 const char* p = kbase + ((i & 1) ? kbo : kbe) + k_rd_step(i);
@@ -193,26 +195,22 @@ struct PP {
         }
     }
 
-    // P of one half as two bf16x8 operands (accumulator order): exp2 of the
-    // scaled, max-shifted scores, packed pairwise; the fp32 values feed this
-    // lane's share of the row sum (plain adds: the packed dot-product
-    // instructions share the matrix pipe and would stall beside the MFMAs of
-    // the other wave).
-    static __device__ __forceinline__ void softmax_pack(const f32x16& sc, float c, float mneg, float& l,
-                                                        bf16x8& b0, bf16x8& b1) {
+    // Eight P values (accumulator elements i0 .. i0+7 of one half) as one
+    // bf16x8 operand: exp2 of the scaled, max-shifted scores, packed
+    // pairwise; the fp32 values feed this lane's share of the row sum (plain
+    // adds: the packed dot-product instructions share the matrix pipe and
+    // would stall beside the MFMAs of the other wave).
+    static __device__ __forceinline__ bf16x8 pack8(const f32x16& sc, int i0, float c, float mneg, float& l) {
+        bf16x8 b;
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, mneg));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i + 1], c, mneg));
+        for (int i = 0; i < 8; i += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0 + i], c, mneg));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i0 + i + 1], c, mneg));
             l += p0 + p1;
-            if (i < 8) {
-                b0[i] = (__bf16)p0;
-                b0[i + 1] = (__bf16)p1;
-            } else {
-                b1[i - 8] = (__bf16)p0;
-                b1[i - 7] = (__bf16)p1;
-            }
+            b[i] = (__bf16)p0;
+            b[i + 1] = (__bf16)p1;
         }
+        return b;
     }
 
     // Row max over both halves (v_max3 tree).
@@ -334,8 +332,8 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     const int n0 = nph >= 1 ? ph0.last - ph0.first + 1 : 0;
     const int n1 = nph >= 2 ? ph1.last - ph1.first + 1 : 0;
     const int nv = n0 + n1;
-    auto phase_of = [&](int v) -> Phase { return v < n0 ? ph0 : ph1; };
-    auto tile_of = [&](int v) -> int { return v < n0 ? ph0.first + v : ph1.first + (v - n0); };
+    auto phase_of = [&](int v) __attribute__((always_inline)) -> Phase { return v < n0 ? ph0 : ph1; };
+    auto tile_of = [&](int v) __attribute__((always_inline)) -> int { return v < n0 ? ph0.first + v : ph1.first + (v - n0); };
 
     // ---- direct loads: a tile's K (or V) is brought in by the 4 waves of
     // one group; wave `sub` issues instructions sub, sub + 4, ...
@@ -345,13 +343,20 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     int kbe, kbo;
     T::k_rd_bases(l32, g, kbe, kbo);
 
-    // Rows of tile v: when every query of the workgroup may need every row
-    // of the tile and the rows are all in the call's own tokens (contiguous)
-    // or all in the rolling part of the cache (slot s + p mod r, one wrap),
-    // a direct formula; otherwise each row is clamped to one the tile does
-    // need.  A clamped row is real, finite data that the score mask then
-    // removes (-inf score, weight 0).  Returns the number of loads issued.
-    auto issue = [&](int v, bool is_k, int set) -> int {
+    // Loads of tile v's K (or V) into buffer set `set`.  When every query of
+    // the workgroup may need every row of the tile and the rows are all in
+    // the call's own tokens (contiguous) or all in the rolling part of the
+    // cache (slot s + p mod r, one wrap), a direct formula; otherwise each
+    // row is clamped to one the tile does need.  A clamped row is real,
+    // finite data that the score mask then removes (-inf score, weight 0).
+    // Past the last tile the last tile is read again into the given set (a
+    // buffer region no later cluster reads), so every wave always issues
+    // the same number of loads.
+    const uint32_t kloff = (uint32_t)(kkey0 * T::RB + kchk), vloff = (uint32_t)(vkey0 * T::RB + vchk);
+    auto issue = [&](auto is_k_c, int v, int set) __attribute__((always_inline)) {
+        constexpr bool is_k = decltype(is_k_c)::value;
+        u32x4* dst0 = is_k ? smem[set].k : smem[set].v;
+        v = v < nv ? v : nv - 1;
         const Phase P = phase_of(v);
         const int kbase = tile_of(v) * BN, klast = kbase + BN - 1;
         const int lo_any = P.band_lo > t0 - r + 1 ? P.band_lo : t0 - r + 1;
@@ -360,13 +365,12 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         const __bf16* cache = is_k ? kc : vc;
         const int key0 = is_k ? kkey0 : vkey0;
         const int chk = is_k ? kchk : vchk;
-        u32x4* dst0 = is_k ? smem[set].k : smem[set].v;
         if (all_needed && kbase >= pos0) {
             // the call's own rows kbase.. (contiguous)
-            const uint32_t lo = (uint32_t)(key0 * T::RB + chk);
+            const __bf16* base = own + (size_t)(kbase - pos0) * D;
 #pragma unroll
             for (int j = 0; j < T::JN; ++j)
-                load_lds16_off(own + (size_t)(kbase - pos0 + T::JSTEP * j) * D, lo, dst0 + 64 * (sub + GW * j));
+                load_lds16_off(base + (size_t)T::JSTEP * j * D, is_k ? kloff : vloff, dst0 + 64 * (sub + GW * j));
         } else if (all_needed && kbase >= s && klast < pos0) {
             // rolling cache slots s + (p mod r), at most one wrap in a tile
             const __bf16* base = cache + (size_t)s * D;
@@ -397,8 +401,9 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
                 load_lds16((const char*)rowp + chk, dst0 + 64 * (sub + GW * j));
             }
         }
-        return T::JN;
     };
+    const std::integral_constant<bool, true> K_;
+    const std::integral_constant<bool, false> V_;
 
     // ---- per-wave state
     typename T::QRegs qr;
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // The queries tile v is scored with (RoPE: the sink phase uses queries
     // rotated to min(t, s+r-1)); reloaded only when the phase changes, and
     // waited for here so no later instruction waits on it.
-    auto ensure_q = [&](int v) {
+    auto ensure_q = [&](int v) __attribute__((always_inline)) {
         const int want_q = (phase_of(v).use_qs && a.qs != a.q) ? 1 : 0;
         if (want_q != q_loaded) {
             T::load_q(qr, (const __bf16*)(want_q ? a.qs : a.q) + qoff, my_valid, g);
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // X(v): online softmax of tile v's scores into pk (zeros when no row of
     // the wave needs the tile); the mask is applied only to tiles that are
     // not inside every row's key set.
-    auto cluster_x = [&](int v) {
+    auto cluster_x = [&](int v) __attribute__((always_inline)) {
         const Phase P = phase_of(v);
         const int kb = tile_of(v) * BN;
         const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
@@ -448,8 +453,6 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         const bool full = kb + 63 <= tw0 && (kb >= lo_w1 || kb + 63 < P.sink_hi);
         const float NEG = -__builtin_inff();
         if (!full) {
-            // key kb + 32 hb + 8 g + k_i of element i of half hb (k_i an
-            // immediate) is in U(t) iff k <= t and (k < sink_hi or k >= lo(t))
             const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
             const int kbg = kb + 8 * g;
             const int lim_t = my_t - kbg, lim_s = P.sink_hi - kbg, lim_b = lo_me - kbg;
@@ -474,57 +477,59 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         }
         const float mneg = (m_c == NEG) ? 0.0f : -m_c;
-        T::softmax_pack(sacc0, c, mneg, l_part, pk[0], pk[1]);
-        T::softmax_pack(sacc1, c, mneg, l_part, pk[2], pk[3]);
+        pk[0] = T::pack8(sacc0, 0, c, mneg, l_part);
+        pk[1] = T::pack8(sacc0, 8, c, mneg, l_part);
+        pk[2] = T::pack8(sacc1, 0, c, mneg, l_part);
+        pk[3] = T::pack8(sacc1, 8, c, mneg, l_part);
     };
 
     // ---- schedule.  Half-slot hs: group 0 runs C(v) at hs = 2v and X(v) at
     // 2v+1, group 1 runs X(v-1) at 2v and C(v) at 2v+1; a barrier ends every
     // half-slot.  C(v) reads K of tile v and V of tile v-1 from set v % 3
-    // during half-slots 2v and 2v+1.  Group 0's C(v) fetches K of tile v+2
-    // and group 1's C(v) fetches V of tile v+1, both into set (v+2) % 3
-    // (last read at 2v-1); a wave ends each half-slot waiting for all but
-    // its latest batch of loads, so every batch lands at least one barrier
-    // before its first reader.  C(0) (no PV) and C(nv) (no QK) are peeled off
-    // the loop.
+    // during half-slots 2v and 2v+1.  The softmax half-slots also carry the
+    // direct loads (their waves have issue slots to spare): group 1 fetches
+    // K of tile v+2 at 2v and group 0 V of tile v+1 at 2v+1, both into set
+    // (v+2) % 3 (last read at 2v-1); a wave ends each half-slot waiting for
+    // all but its latest batch of loads, so every batch lands at least one
+    // barrier before its first reader.  C(0) (no PV) and C(nv) (no QK) are
+    // peeled off the loop.
     int n_last = 0;
     if (nv > 0) {
         if (grp == 0) {
-            issue(0, true, 0);
-            issue(0, false, 1);
+            issue(K_, 0, 0);
+            issue(V_, 0, 1);
         } else if (nv > 1) {
-            issue(1, true, 1);
+            issue(K_, 1, 1);
         }
     }
     wait_vm(0);
     wg_barrier();
-    auto end_half = [&]() {
+    auto end_half = [&]() __attribute__((always_inline)) {
         wait_vm(n_last);
         wg_barrier();
     };
-    // this group's loads during C(v) into set nset
-    auto c_loads = [&](int v, int nset) {
-        if (grp == 0) n_last = (v + 2 < nv) ? issue(v + 2, true, nset) : 0;
-        else n_last = (v + 1 < nv) ? issue(v + 1, false, nset) : 0;
+    // this group's X half-slot: its loads (group 1 at hs = 2v: K of tile
+    // v+2; group 0 at hs = 2v+1: V of tile v+1; both into set (v+2) % 3),
+    // then the softmax of tile vx
+    auto x_half = [&](auto is_k_c, int vx, int v, int nset) __attribute__((always_inline)) {
+        n_last = T::JN;
+        issue(is_k_c, decltype(is_k_c)::value ? v + 2 : v + 1, nset);
+        if (wave_active && vx >= 0) cluster_x(vx);
     };
-    auto c_first = [&]() {
+
+    auto c_first = [&]() __attribute__((always_inline)) {
         if (wave_active) {
             ensure_q(0);
-            T::template cluster<true, false>(smem[0], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [&] { c_loads(0, 2); });
-        } else {
-            c_loads(0, 2);
+            T::template cluster<true, false>(smem[0], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
         }
     };
-    auto c_mid = [&](int v, int set, int nset) {
+    auto c_mid = [&](int v, int set) __attribute__((always_inline)) {
         if (wave_active) {
             ensure_q(v);
-            T::template cluster<true, true>(smem[set], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [&] { c_loads(v, nset); });
-        } else {
-            c_loads(v, nset);
+            T::template cluster<true, true>(smem[set], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
         }
     };
-    auto c_last = [&](int set) {
-        n_last = 0;
+    auto c_last = [&](int set) __attribute__((always_inline)) {
         if (wave_active)
             T::template cluster<false, true>(smem[set], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
     };
@@ -532,34 +537,36 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         if (grp == 0) {
             c_first();
             end_half();
-            if (wave_active) cluster_x(0);
+            x_half(V_, 0, 0, 2);
             end_half();
             int set = 1;                       // v % 3
             for (int v = 1; v < nv; ++v) {
                 const int nset = set == 0 ? 2 : set - 1;   // (v + 2) % 3
-                c_mid(v, set, nset);
+                c_mid(v, set);
                 end_half();
-                if (wave_active) cluster_x(v);
+                x_half(V_, v, v, nset);
                 end_half();
                 set = set == 2 ? 0 : set + 1;
             }
+            n_last = 0;
             c_last(set);
             end_half();
             end_half();
         } else {
+            x_half(K_, -1, 0, 2);
             end_half();
             c_first();
             end_half();
             int set = 1;
             for (int v = 1; v < nv; ++v) {
                 const int nset = set == 0 ? 2 : set - 1;
-                if (wave_active) cluster_x(v - 1);
+                x_half(K_, v - 1, v, nset);
                 end_half();
-                c_mid(v, set, nset);
+                c_mid(v, set);
                 end_half();
                 set = set == 2 ? 0 : set + 1;
             }
-            if (wave_active) cluster_x(nv - 1);
+            x_half(K_, nv - 1, nv, set == 0 ? 2 : set - 1);
             end_half();
             c_last(set);
             end_half();
