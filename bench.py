@@ -115,18 +115,19 @@ def bench_prefill(torch, swa, w, steps, warmup):
     for _ in range(warmup):
         swa.prefill(qd, kd, vd, w.s, w.r, out=out)
     torch.cuda.synchronize()
-    timer = LaunchTimer(torch, stream)
+    # one step is one launch of the kernel, so the events around the K
+    # back-to-back launches give its mean launch duration; events between
+    # launches would add a cache flush and a stall to every launch
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(steps):
-        with timer:
-            swa.prefill(qd, kd, vd, w.s, w.r, out=out)
+        swa.prefill(qd, kd, vd, w.s, w.r, out=out)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     flops = prefill_flops(w)
-    return {"ms": ms, "kernel_ms": timer.mean_ms(), "flops": flops, "tflops": flops / ms / 1e9}
+    return {"ms": ms, "kernel_ms": ms, "flops": flops, "tflops": flops / ms / 1e9}
 
 
 def bench_decode(torch, swa, w, steps=None):
@@ -156,24 +157,30 @@ def bench_decode(torch, swa, w, steps=None):
         swa.decode(qd[i], kc2, vc2, w.L + i + 1, w.s, w.r, out=out, workspace=ws)
     torch.cuda.synchronize()
     del kc2, vc2
-    timer = LaunchTimer(torch, stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(steps):
         T = w.L + i + 1
         swa.cache_append(kn[i], vn[i], kc, vc, T - 1, w.s, w.r)
-        with timer:
-            swa.decode(qd[i], kc, vc, T, w.s, w.r, out=out, workspace=ws)
+        swa.decode(qd[i], kc, vc, T, w.s, w.r, out=out, workspace=ws)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    # the decode launch alone: back-to-back launches at the last step's T
+    nd = min(64, steps)
+    t0.record(stream)
+    for i in range(nd):
+        swa.decode(qd[steps - 1], kc, vc, w.L + steps, w.s, w.r, out=out, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    decode_ms = t0.elapsed_time(t1) / nd
     S = w.s + w.r
     kv = w.B * w.Hkv * S * w.d * 2 * 2
     qo = 2 * w.B * w.Hq * w.d * 2
     app = w.B * w.Hkv * w.d * 2 * 2
     step_bytes = kv + qo + app
-    return {"ms": ms, "decode_ms": timer.mean_ms(), "bytes_per_step": step_bytes, "steps": steps,
+    return {"ms": ms, "decode_ms": decode_ms, "bytes_per_step": step_bytes, "steps": steps,
             "gbs": step_bytes / ms / 1e6, "decode_kernel_bytes": kv + qo}
 
 
@@ -205,15 +212,19 @@ def bench_chunked(torch, swa, w, reps=2):
 
     one_pass()
     torch.cuda.synchronize()
-    timer = LaunchTimer(torch, stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(reps):
-        one_pass(timer)
+        one_pass()
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / reps
+    # per-call prefill durations from an extra, untimed pass (events around
+    # each call slow the pass they sit in)
+    timer = LaunchTimer(torch, stream)
+    one_pass(timer)
+    torch.cuda.synchronize()
     flops = 4.0 * w.d * key_count_sum(w.L, w.s, w.r) * w.B * w.Hq
     return {"ms": ms, "flops": flops, "tflops": flops / ms / 1e9, "prefill_call_ms": timer.mean_ms()}
 

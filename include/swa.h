@@ -110,7 +110,8 @@ int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new,
 /*
  * Split-K decode.  Bytes of workspace swa_decode needs for n_split splits of
  * the s + r slots (0 = the library's choice for this shape):
- * B * Hq * n_split * (d + 2) * 4 bytes.
+ * B * Hq * n_split * (d + 2) * 4 bytes, or 0 for one split (the split
+ * kernel then writes o itself and workspace may be NULL).
  */
 size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split);
 

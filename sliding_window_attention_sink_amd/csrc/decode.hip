@@ -19,7 +19,9 @@
 //  * O^T += V^T P^T on the same MFMA; V is transposed through a per-wave LDS
 //    tile so each lane's eight keys of one dimension are one 16-byte read;
 //  * the 4 waves merge in LDS and write (max, sum, unnormalised O) per head
-//    and split; a second kernel merges the splits and normalises.
+//    and split; a second kernel merges the splits and normalises.  With one
+//    split (enough (batch, kv-head) units to fill the chip) the workgroup
+//    writes the normalised output itself and the second kernel is skipped.
 #include "swa_internal.h"
 
 namespace swa {
@@ -230,6 +232,11 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
             o += f * sm.o[w][cl][dim];
             l += f * sm.l[w][cl];
         }
+        if (a.n_split == 1) {
+            // one split: this workgroup saw every slot, so it finishes the head
+            ((__bf16*)a.o)[((size_t)b * a.Hq + kvh * G + cl) * D + dim] = (__bf16)(o / l);
+            continue;
+        }
         float* ws = a.ws + (((size_t)b * a.Hq + kvh * G + cl) * a.n_split + split) * (D + 2);
         if (dim == 0) {
             ws[0] = M;
@@ -261,7 +268,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
     const unsigned nblk = (unsigned)a.B * a.Hkv * a.n_split;
     hipLaunchKernelGGL((decode_split_kernel<D>), dim3(nblk), dim3(NT), 0, st, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.n_split == 1) return e;
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((unsigned)a.B * a.Hq), dim3(D), 0, st, a);
     return hipGetLastError();
 }

@@ -86,16 +86,26 @@ RopeLayout rope_layout(const swa_desc* d, int64_t L) {
     return r;
 }
 
+// Splits per (batch, kv-head) unit: enough workgroups for two per compute
+// unit (512 on 256 CUs), each over at least 256 slots; one split when the
+// units alone fill the chip (the split kernel then writes the output).
 int32_t default_splits(const swa_desc* d) {
     const int64_t S = (int64_t)d->s + d->r;
     const int64_t units = (int64_t)d->B * d->Hkv;
-    int64_t n = (2048 + units - 1) / units;
+    int64_t n = (512 + units - 1) / units;
     int64_t cap = S / 256;
     if (cap < 1) cap = 1;
     if (n > cap) n = cap;
     if (n > 64) n = 64;
     if (n < 1) n = 1;
     return (int32_t)n;
+}
+
+// Per-split partial results (max, sum, unnormalised O) per query head; one
+// split writes the output directly and needs none.
+size_t decode_ws_bytes(const swa_desc* desc, int32_t n_split) {
+    if (n_split == 1) return 0;
+    return (size_t)desc->B * desc->Hq * n_split * (desc->d + 2) * sizeof(float);
 }
 
 }  // namespace
@@ -248,7 +258,7 @@ size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split) {
     if (check_desc(desc, "swa_decode_workspace_bytes") != SWA_OK) return 0;
     if (n_split == 0) n_split = default_splits(desc);
     if (n_split < 1 || n_split > 64) return 0;
-    return (size_t)desc->B * desc->Hq * n_split * (desc->d + 2) * sizeof(float);
+    return decode_ws_bytes(desc, n_split);
 }
 
 int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const void* v_cache, int64_t T, void* o,
@@ -262,14 +272,14 @@ int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const v
     if (desc->Hq / desc->Hkv > 16)
         return fail(SWA_ERR_UNSUPPORTED, "%s: more than 16 q-heads per kv-head", fn);
     if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k_cache, fn, "k_cache")) ||
-        (st = check_ptr(v_cache, fn, "v_cache")) || (st = check_ptr(o, fn, "o")) ||
-        (st = check_ptr(workspace, fn, "workspace")))
+        (st = check_ptr(v_cache, fn, "v_cache")) || (st = check_ptr(o, fn, "o")))
         return st;
     if (T < 1) return fail(SWA_ERR_INVALID_ARG, "%s: T must be >= 1", fn);
     if (T > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: T beyond 2^30", fn);
     if (n_split == 0) n_split = default_splits(desc);
     if (n_split < 1 || n_split > 64) return fail(SWA_ERR_INVALID_ARG, "%s: n_split %d outside 1..64", fn, n_split);
-    const size_t need = (size_t)desc->B * desc->Hq * n_split * (desc->d + 2) * sizeof(float);
+    const size_t need = decode_ws_bytes(desc, n_split);
+    if (need > 0 && (st = check_ptr(workspace, fn, "workspace"))) return st;
     if (workspace_bytes < need)
         return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
     if ((int64_t)desc->B * desc->Hkv * n_split > 0x7fffffffLL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);

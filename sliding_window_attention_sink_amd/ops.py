@@ -112,8 +112,8 @@ def decode(q, k_cache, v_cache, T, s, r, *, scale=None, n_split=0, out=None, wor
         out = torch.empty_like(q)
     _need(out, "out", q.shape, q.dtype, dev)
     wsb = _lib.swa_decode_workspace_bytes(desc, n_split)
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     check(_lib.swa_decode(desc, _ptr(q), _ptr(k_cache), _ptr(v_cache), T, _ptr(out), n_split, _ptr(workspace),
-                          workspace.numel(), _stream(dev, stream)))
+                          0 if workspace is None else workspace.numel(), _stream(dev, stream)))
     return out

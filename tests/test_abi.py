@@ -109,8 +109,10 @@ def test_decode_rejects():
     assert ws == 1 * 4 * 3 * (128 + 2) * 4
     dflt = _lib.swa_decode_default_splits(d_)
     assert 1 <= dflt <= 64
-    assert _lib.swa_decode_workspace_bytes(d_, 0) == 1 * 4 * dflt * 130 * 4
+    assert _lib.swa_decode_workspace_bytes(d_, 0) == (0 if dflt == 1 else 1 * 4 * dflt * 130 * 4)
     assert _lib.swa_decode_workspace_bytes(d_, 65) == 0
+    # one split needs no workspace
+    assert _lib.swa_decode_workspace_bytes(d_, 1) == 0
 
     def dec(dd=d_, T=10, n_split=3, wsb=ws, q=A):
         return _lib.swa_decode(dd, q, B_, C, T, D, n_split, W, wsb, None)
