@@ -224,7 +224,16 @@ struct PP {
         return fmaxf(m, y[15]);
     }
 
-    static __device__ __forceinline__ void store_o(__bf16* row, const f32x16* o, float inv, int g) {
+    // Epilogue of one wave: its 32 normalised output rows go to LDS as bf16
+    // (row stride RB + 16 bytes, so the 32 rows of one write start in
+    // different banks), then to HBM as whole rows, 16 bytes per lane and
+    // 64 / (RB / 16) rows per instruction (scattered 8-byte writes of the
+    // O^T accumulator layout straight to HBM cost several microseconds per
+    // workgroup).  Rows from nvalid on are not stored.
+    static constexpr int ORS = RB + 16;
+    static __device__ __forceinline__ void store_o(char* lds, __bf16* orow0, const f32x16* o, float inv, int lane,
+                                                   int nvalid) {
+        const int row = lane & 31, g = lane >> 5;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -236,8 +245,19 @@ struct PP {
                 u32x2 w;
                 w[0] = v0 | (v1 << 16);
                 w[1] = v2 | (v3 << 16);
-                *(u32x2*)(row + 32 * db + 8 * q4 + 4 * g) = w;
+                *(u32x2*)(lds + row * ORS + 2 * (32 * db + 8 * q4 + 4 * g)) = w;
             }
+        }
+        // LDS accesses of one wave complete in order; the empty asm keeps
+        // the compiler from moving the reads above the writes
+        asm volatile("" ::: "memory");
+        constexpr int CPR = RB / 16, RPI = 64 / CPR;
+        const int rr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+        for (int i = 0; i < WROWS / RPI; ++i) {
+            const int r = RPI * i + rr;
+            const u32x4 x = *(const u32x4*)(lds + r * ORS + 16 * cc);
+            if (r < nvalid) *(u32x4*)((char*)orow0 + (size_t)r * RB + 16 * cc) = x;
         }
     }
 };
@@ -573,10 +593,15 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         }
     }
 
+    // the buffers take the output rows once every load has landed and every
+    // wave is past its last read
+    wait_vm(0);
+    wg_barrier();
     if (!wave_active) return;
     const float l_tot = l_part + __shfl_xor(l_part, 32);
-    if (!my_valid) return;
-    T::store_o((__bf16*)a.o + qoff, oacc, 1.0f / l_tot, g);
+    static_assert(PW * WROWS * T::ORS <= (int)sizeof(smem), "output staging fits the tile buffers");
+    T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * D, oacc,
+               my_valid ? 1.0f / l_tot : 0.0f, lane, tw1 - tw0 + 1);
 }
 
 template <int D>
