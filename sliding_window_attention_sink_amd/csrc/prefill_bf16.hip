@@ -29,9 +29,11 @@
 // share it), so the row max is one v_permlane32_swap exchange; K rows enter
 // the MFMA in a permuted order so that each lane's eight P values are eight
 // consecutive keys, which makes the accumulator itself the P^T operand.  V
-// stays row-major in LDS and ds_read_b64_tr_b16 delivers it transposed.  The
-// running max is raised only when a tile's max exceeds it by more than 2^8
-// (exact: the same max scales the numerator and the denominator).
+// stays row-major in LDS and ds_read_b64_tr_b16 delivers it transposed.  A
+// tile's weights are first taken against the running max; only when some
+// lane's weights of the tile sum past 2^8 (or a row has no max yet) is the
+// exact row max taken and the running state rescaled (exact either way: the
+// same max scales the numerator and the denominator).
 #include <type_traits>
 
 #include "prefill_common.h"
@@ -152,7 +154,7 @@ struct PP {
     template <bool QK, bool PV, class Mid>
     static __device__ __forceinline__ void cluster(const Buf& S, const QRegs& Q, const int* vb, const bf16x8* pk,
                                                    int kbe, int kbo, f32x16& a0, f32x16& a1, f32x16* o, Mid&& mid) {
-        constexpr int LA = 2;
+        constexpr int LA = 1;
         constexpr int R = QK_STEPS;
         const char* kbase = (const char*)S.k;
         u32x4 ka[LA + 1], kb[LA + 1];
@@ -213,15 +215,17 @@ struct PP {
         return b;
     }
 
-    // Row max over both halves (v_max3 tree).
+    // Row max over both halves: four independent v_max3 chains of eight
+    // values each, then their max (depth 6 instead of 16).
+    static __device__ __forceinline__ float max8(const f32x16& x, int i) {
+        float m = fmaxf(fmaxf(x[i], x[i + 1]), x[i + 2]);
+        m = fmaxf(fmaxf(m, x[i + 3]), x[i + 4]);
+        m = fmaxf(fmaxf(m, x[i + 5]), x[i + 6]);
+        return fmaxf(m, x[i + 7]);
+    }
     static __device__ __forceinline__ float max2x16(const f32x16& x, const f32x16& y) {
-        float m = fmaxf(fmaxf(x[0], x[1]), x[2]);
-#pragma unroll
-        for (int i = 3; i < 15; i += 2) m = fmaxf(fmaxf(m, x[i]), x[i + 1]);
-        m = fmaxf(fmaxf(m, x[15]), y[0]);
-#pragma unroll
-        for (int i = 1; i < 15; i += 2) m = fmaxf(fmaxf(m, y[i]), y[i + 1]);
-        return fmaxf(m, y[15]);
+        const float m0 = max8(x, 0), m1 = max8(x, 8), m2 = max8(y, 0), m3 = max8(y, 8);
+        return fmaxf(fmaxf(fmaxf(m0, m1), m2), m3);
     }
 
     // Epilogue of one wave: its 32 normalised output rows go to LDS as bf16
@@ -483,24 +487,43 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
                 sacc1[i] = (k1 <= lim_t && (k1 < lim_s || k1 >= lim_b)) ? sacc1[i] : NEG;
             }
         }
-        float mx = T::max2x16(sacc0, sacc1);
-        mx = max_pair_lanes(mx);
-        const float mxc = mx * c;
-        const bool upd = mxc > m_c + RESCALE_TH;
-        if (__builtin_amdgcn_ballot_w64(upd)) {
-            const float alpha = upd ? __builtin_amdgcn_exp2f(m_c - mxc) : 1.0f;
-            m_c = upd ? mxc : m_c;
-            l_part *= alpha;
-#pragma unroll
-            for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        // P against the running max first: while this lane's weights of the
+        // tile sum to at most 2^8 (so each is at most 2^8, as the lazily
+        // raised max allows anyway) they stand and the tile needs no row
+        // max.  Otherwise, and while a row has no running max yet, the exact
+        // row max is taken, the running state rescaled and P recomputed.
+        float t = 0.0f;
+        bool slow = __builtin_amdgcn_ballot_w64(m_c == NEG) != 0;
+        if (!slow) {
+            const float mneg = -m_c;
+            pk[0] = T::pack8(sacc0, 0, c, mneg, t);
+            pk[1] = T::pack8(sacc0, 8, c, mneg, t);
+            pk[2] = T::pack8(sacc1, 0, c, mneg, t);
+            pk[3] = T::pack8(sacc1, 8, c, mneg, t);
+            slow = __builtin_amdgcn_ballot_w64(!(t <= 256.0f)) != 0;
         }
-        const float mneg = (m_c == NEG) ? 0.0f : -m_c;
-        pk[0] = T::pack8(sacc0, 0, c, mneg, l_part);
-        pk[1] = T::pack8(sacc0, 8, c, mneg, l_part);
-        pk[2] = T::pack8(sacc1, 0, c, mneg, l_part);
-        pk[3] = T::pack8(sacc1, 8, c, mneg, l_part);
+        if (slow) {
+            float mx = T::max2x16(sacc0, sacc1);
+            mx = max_pair_lanes(mx);
+            const float mxc = mx * c;
+            const bool upd = mxc > m_c;
+            if (__builtin_amdgcn_ballot_w64(upd)) {
+                const float alpha = upd ? __builtin_amdgcn_exp2f(m_c - mxc) : 1.0f;
+                m_c = upd ? mxc : m_c;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            }
+            const float mneg = (m_c == NEG) ? 0.0f : -m_c;
+            t = 0.0f;
+            pk[0] = T::pack8(sacc0, 0, c, mneg, t);
+            pk[1] = T::pack8(sacc0, 8, c, mneg, t);
+            pk[2] = T::pack8(sacc1, 0, c, mneg, t);
+            pk[3] = T::pack8(sacc1, 8, c, mneg, t);
+        }
+        l_part += t;
     };
 
     // ---- schedule.  Half-slot hs: group 0 runs C(v) at hs = 2v and X(v) at
