@@ -9,7 +9,7 @@ line's value is its algorithmic TFLOP/s: only the (query, key) pairs of the
 sink + window key set count, 4*d flops each.  Alongside it (under "extra")
 the same run times the StreamingLLM 4+1020 prefill (B=4, H=32, L=16384), the
 rolling-buffer decode loop (B=64, 32/8 heads, 4+4092 slots, append + decode
-per step) and the chunked RoPE streaming prefill (131072 tokens in chunks of
+per step, as one fused launch and as two) and the chunked RoPE streaming prefill (131072 tokens in chunks of
 4096).  The "cpu_baseline" leg times the fp64 oracle on a bounded sample of
 the main workload's rows.
 
@@ -159,11 +159,23 @@ def bench_decode(torch, swa, w, steps=None):
     del kc2, vc2
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    # the same steps as separate append and decode launches, on a copy of
+    # the cache (for comparison; not the reported step time)
+    kc3, vc3 = kc.clone(), vc.clone()
     t0.record(stream)
     for i in range(steps):
         T = w.L + i + 1
-        swa.cache_append(kn[i], vn[i], kc, vc, T - 1, w.s, w.r)
-        swa.decode(qd[i], kc, vc, T, w.s, w.r, out=out, workspace=ws)
+        swa.cache_append(kn[i], vn[i], kc3, vc3, T - 1, w.s, w.r)
+        swa.decode(qd[i], kc3, vc3, T, w.s, w.r, out=out, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_separate = t0.elapsed_time(t1) / steps
+    del kc3, vc3
+    knd = [kd[i] for i in range(steps)]
+    vnd = [vd[i] for i in range(steps)]
+    t0.record(stream)
+    for i in range(steps):
+        swa.decode_step(qd[i], knd[i], vnd[i], kc, vc, w.L + i + 1, w.s, w.r, out=out, workspace=ws)
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
@@ -180,7 +192,7 @@ def bench_decode(torch, swa, w, steps=None):
     qo = 2 * w.B * w.Hq * w.d * 2
     app = w.B * w.Hkv * w.d * 2 * 2
     step_bytes = kv + qo + app
-    return {"ms": ms, "decode_ms": decode_ms, "bytes_per_step": step_bytes, "steps": steps,
+    return {"ms": ms, "ms_separate": ms_separate, "decode_ms": decode_ms, "bytes_per_step": step_bytes, "steps": steps,
             "gbs": step_bytes / ms / 1e6, "decode_kernel_bytes": kv + qo}
 
 
@@ -308,6 +320,7 @@ def main():
         r4 = bench_decode(torch, swa, w4, args.decode_steps)
         dec_gbs = r4["decode_kernel_bytes"] / r4["decode_ms"] / 1e6
         extra[w4.name] = {"GB/s": r4["gbs"], "us_per_step": r4["ms"] * 1e3, "steps": r4["steps"],
+                          "us_per_step_separate_append_decode": r4["ms_separate"] * 1e3,
                           "bytes_per_step": r4["bytes_per_step"], "frac_hbm_peak": r4["gbs"] / PEAK_HBM_GBS,
                           "decode_launch_us": r4["decode_ms"] * 1e3, "decode_launch_GB/s": dec_gbs,
                           "decode_launch_frac_hbm_peak": dec_gbs / PEAK_HBM_GBS}

@@ -128,6 +128,20 @@ size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split);
 int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const void* v_cache, int64_t T,
                void* o, int32_t n_split, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One generation step in one launch: appends token T-1 (k_new, v_new:
+ * [B, Hkv, d], the same bytes swa_cache_append would take with n = 1,
+ * pos0 = T-1) to the cache and decodes its query q over the cache holding
+ * tokens 0 .. T-1.  The result and the cache afterwards equal those of
+ * swa_cache_append followed by swa_decode (the token is read from k_new /
+ * v_new, and written to its slot, in the same kernel); workspace as for
+ * swa_decode.  Errors: those of swa_decode, and SWA_ERR_INVALID_ARG for a
+ * null or misaligned k_new / v_new.
+ */
+int swa_decode_step(const swa_desc* desc, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, int64_t T, void* o, int32_t n_split, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* The split count swa_decode uses for n_split = 0. */
 int32_t swa_decode_default_splits(const swa_desc* desc);
 

@@ -7,6 +7,8 @@ of include/swa.h); this package binds it for PyTorch callers:
                                        rolling cache (chunked) and RoPE
   * cache_append(k, v, kc, vc, pos0, ...) write tokens into the rolling cache
   * decode(q, kc, vc, T, s, r, ...)    split-K single-query decode
+  * decode_step(q, k, v, kc, vc, T, s, r, ...) append token T-1 and decode
+                                       it in one launch
 
 The low-level same-name wrappers of the C functions are in ``_lib``.
 """
@@ -14,6 +16,7 @@ from ._lib import EXPORTS, LIB_PATH, SwaDesc, SwaError, load  # noqa: F401
 from .ops import (  # noqa: F401
     cache_append,
     decode,
+    decode_step,
     decode_workspace_bytes,
     make_desc,
     new_cache,

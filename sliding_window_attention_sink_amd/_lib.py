@@ -22,7 +22,8 @@ SWA_BF16 = 1
 # every symbol include/swa.h declares
 EXPORTS = (
     "swa_prefill_workspace_bytes", "swa_prefill", "swa_cache_append", "swa_decode_workspace_bytes",
-    "swa_decode", "swa_decode_default_splits", "swa_status_str", "swa_last_error", "swa_abi_version",
+    "swa_decode", "swa_decode_step", "swa_decode_default_splits", "swa_status_str", "swa_last_error",
+    "swa_abi_version",
 )
 
 
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.swa_decode_workspace_bytes.restype = sz
     lib.swa_decode.argtypes = [dp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
     lib.swa_decode.restype = ctypes.c_int
+    lib.swa_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
+    lib.swa_decode_step.restype = ctypes.c_int
     lib.swa_decode_default_splits.argtypes = [dp]
     lib.swa_decode_default_splits.restype = i32
     lib.swa_status_str.argtypes = [ctypes.c_int]
@@ -107,6 +110,12 @@ def swa_decode_default_splits(desc: SwaDesc) -> int:
 def swa_decode(desc, q, k_cache, v_cache, T, o, n_split, workspace, workspace_bytes, stream) -> int:
     return load().swa_decode(ctypes.byref(desc), q, k_cache, v_cache, T, o, n_split, workspace,
                              workspace_bytes, stream)
+
+
+def swa_decode_step(desc, q, k_new, v_new, k_cache, v_cache, T, o, n_split, workspace, workspace_bytes,
+                    stream) -> int:
+    return load().swa_decode_step(ctypes.byref(desc), q, k_new, v_new, k_cache, v_cache, T, o, n_split, workspace,
+                                  workspace_bytes, stream)
 
 
 def swa_status_str(status: int) -> str:

@@ -22,6 +22,10 @@
 //    and split; a second kernel merges the splits and normalises.  With one
 //    split (enough (batch, kv-head) units to fill the chip) the workgroup
 //    writes the normalised output itself and the second kernel is skipped.
+//  * fused step (kn/vn given): the workgroup whose slot range holds the
+//    current token's slot first writes the token's K/V row there (then
+//    waits for the stores and a barrier), so one launch does the append and
+//    the decode.
 #include "swa_internal.h"
 
 namespace swa {
@@ -81,6 +85,19 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
 
     const __bf16* kc = (const __bf16*)a.kc + (size_t)bh * S * D;
     const __bf16* vc = (const __bf16*)a.vc + (size_t)bh * S * D;
+    if (a.j_new >= 0 && split == a.j_new / a.slots_per_split) {
+        // fused append: the workgroup whose slot range holds the current
+        // token's slot writes its row there, and every wave reads the slot
+        // only after the stores are complete and the workgroup barrier
+        if (wave == 0 && lane < 2 * CH) {
+            const int c = lane % CH;
+            const bool is_v = lane >= CH;
+            const u32x4* src = (const u32x4*)((const __bf16*)(is_v ? a.vn : a.kn) + (size_t)bh * D);
+            ((u32x4*)((__bf16*)(is_v ? a.vc : a.kc) + ((size_t)bh * S + a.j_new) * D))[c] = src[c];
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores have completed
+        __syncthreads();
+    }
     const int64_t T = a.T;
     const bool all_valid = T >= (int64_t)S;
     // slot j holds a token: sinks j < min(s, T); rolling slot s + q holds the

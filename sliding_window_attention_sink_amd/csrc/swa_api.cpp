@@ -261,9 +261,14 @@ size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split) {
     return decode_ws_bytes(desc, n_split);
 }
 
-int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const void* v_cache, int64_t T, void* o,
-               int32_t n_split, void* workspace, size_t workspace_bytes, void* stream) {
-    static const char* fn = "swa_decode";
+}  // extern "C"
+
+namespace {
+
+// swa_decode, and with k_new/v_new swa_decode_step (append fused in).
+int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void* k_new, const void* v_new,
+                const void* k_cache, const void* v_cache, int64_t T, void* o, int32_t n_split, void* workspace,
+                size_t workspace_bytes, void* stream) {
     clear_error();
     int st = check_desc(desc, fn);
     if (st) return st;
@@ -274,6 +279,8 @@ int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const v
     if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k_cache, fn, "k_cache")) ||
         (st = check_ptr(v_cache, fn, "v_cache")) || (st = check_ptr(o, fn, "o")))
         return st;
+    const bool fused = k_new != nullptr || v_new != nullptr;
+    if (fused && ((st = check_ptr(k_new, fn, "k_new")) || (st = check_ptr(v_new, fn, "v_new")))) return st;
     if (T < 1) return fail(SWA_ERR_INVALID_ARG, "%s: T must be >= 1", fn);
     if (T > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: T beyond 2^30", fn);
     if (n_split == 0) n_split = default_splits(desc);
@@ -293,7 +300,10 @@ int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const v
     a.vc = v_cache;
     a.o = o;
     a.ws = static_cast<float*>(workspace);
+    a.kn = fused ? k_new : nullptr;
+    a.vn = fused ? v_new : nullptr;
     a.T = T;
+    a.j_new = !fused ? -1 : (T - 1 < desc->s) ? (int32_t)(T - 1) : desc->s + (int32_t)((T - 1) % desc->r);
     a.B = desc->B;
     a.Hq = desc->Hq;
     a.Hkv = desc->Hkv;
@@ -303,6 +313,27 @@ int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const v
     a.slots_per_split = sps;
     a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
     return hip_status(swa::launch_decode_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const void* v_cache, int64_t T, void* o,
+               int32_t n_split, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl("swa_decode", desc, q, nullptr, nullptr, k_cache, v_cache, T, o, n_split, workspace,
+                       workspace_bytes, stream);
+}
+
+int swa_decode_step(const swa_desc* desc, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, int64_t T, void* o, int32_t n_split, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    if (k_new == nullptr || v_new == nullptr) {
+        clear_error();
+        return fail(SWA_ERR_INVALID_ARG, "swa_decode_step: k_new and v_new are required");
+    }
+    return decode_impl("swa_decode_step", desc, q, k_new, v_new, k_cache, v_cache, T, o, n_split, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

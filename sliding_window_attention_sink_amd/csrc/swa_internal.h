@@ -49,7 +49,10 @@ struct DecodeArgs {
     const void* vc;
     void* o;            // [B, Hq, d]
     float* ws;          // [B, Hq, n_split, d + 2]: m (log2 units), l, o[d]
+    const void* kn;     // null, or token T-1's K [B, Hkv, d], written to slot j_new first
+    const void* vn;     // same for V
     int64_t T;          // tokens in the cache including the current one
+    int32_t j_new;      // cache slot of token T-1 with kn/vn, else -1
     int32_t B, Hq, Hkv, s, r;
     int32_t n_split;
     int32_t slots_per_split;

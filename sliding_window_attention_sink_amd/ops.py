@@ -117,3 +117,26 @@ def decode(q, k_cache, v_cache, T, s, r, *, scale=None, n_split=0, out=None, wor
     check(_lib.swa_decode(desc, _ptr(q), _ptr(k_cache), _ptr(v_cache), T, _ptr(out), n_split, _ptr(workspace),
                           0 if workspace is None else workspace.numel(), _stream(dev, stream)))
     return out
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, T, s, r, *, scale=None, n_split=0, out=None, workspace=None,
+                stream=None):
+    """Append token T-1 (k_new/v_new [B,Hkv,d]) and decode its query q [B,Hq,d], in one launch."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    dev = q.device
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale)
+    _need(k_new, "k_new", (B, Hkv, d), q.dtype, dev)
+    _need(v_new, "v_new", (B, Hkv, d), q.dtype, dev)
+    _need(k_cache, "k_cache", (B, Hkv, s + r, d), q.dtype, dev)
+    _need(v_cache, "v_cache", (B, Hkv, s + r, d), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.shape, q.dtype, dev)
+    wsb = _lib.swa_decode_workspace_bytes(desc, n_split)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    check(_lib.swa_decode_step(desc, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), T, _ptr(out),
+                               n_split, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                               _stream(dev, stream)))
+    return out

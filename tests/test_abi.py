@@ -126,6 +126,20 @@ def test_decode_rejects():
     assert dec(dd=desc(Hq=34, Hkv=2)) == -2 and "16 q-heads" in _lib.swa_last_error()
 
 
+def test_decode_step_rejects():
+    d_ = desc()
+    ws = _lib.swa_decode_workspace_bytes(d_, 3)
+
+    def step(kn=A, vn=B_, T=10, wsb=ws):
+        return _lib.swa_decode_step(d_, A, kn, vn, C, D, T, W, 3, W, wsb, None)
+
+    assert step(kn=None) == -1 and "k_new" in _lib.swa_last_error()
+    assert step(vn=None) == -1 and "v_new" in _lib.swa_last_error()
+    assert step(kn=A + 4) == -1 and "aligned" in _lib.swa_last_error()
+    assert step(T=0) == -1 and "T must be" in _lib.swa_last_error()
+    assert step(wsb=ws - 4) == -1 and "workspace" in _lib.swa_last_error()
+
+
 def test_last_error_is_per_call():
     assert prefill(desc(r=0)) == -1
     assert _lib.swa_last_error() != ""

@@ -80,6 +80,40 @@ def test_decode_steps_match_oracle(gpu, B, Hq, Hkv, d, s, r, n_split):
     assert err <= TOL["bf16"], f"max-abs error {err}"
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,d,s,r,n_split", [
+    (2, 8, 2, 128, 4, 60, 0),
+    (1, 4, 2, 64, 3, 40, 3),
+    (1, 2, 1, 128, 70, 30, 1),
+])
+def test_decode_step_equals_append_then_decode(gpu, B, Hq, Hkv, d, s, r, n_split):
+    """The fused step gives the bytes of cache_append + decode: outputs and
+    caches bit-identical at every T (sink slots, filling, wrapped), and the
+    outputs match the oracle."""
+    import sliding_window_attention_sink_amd as swa
+    steps = 2 * (s + r) + 10
+    g = np.random.default_rng(B * 1000 + Hq + d + s + r)
+    K = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    V = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    Q = si.round_bf16(g.standard_normal((B, Hq, steps, d)).astype(np.float32))
+    kc1, vc1 = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    kc2, vc2 = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    Kd, Vd, Qd = dev(K, "bf16"), dev(V, "bf16"), dev(Q, "bf16")
+    o1 = torch.empty((steps, B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    say("decode step fused", B, Hq, Hkv, d, s, r, n_split)
+    for t in range(steps):
+        kt, vt, qt = Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous(), Qd[:, :, t].contiguous()
+        swa.cache_append(kt.unsqueeze(2), vt.unsqueeze(2), kc1, vc1, t, s, r)
+        swa.decode(qt, kc1, vc1, t + 1, s, r, n_split=n_split, out=o1[t])
+        swa.decode_step(qt, kt, vt, kc2, vc2, t + 1, s, r, n_split=n_split, out=o2[t])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2))
+    assert np.array_equal(bits(kc1), bits(kc2)) and np.array_equal(bits(vc1), bits(vc2))
+    rows = np.array([[b, h, t] for t in range(steps) for b in range(B) for h in range(Hq)])
+    ref = oracle.prefill_rows(Q, K, V, s, r, rows=rows).reshape(steps, B, Hq, d)
+    assert max_err(host(o2), ref) <= TOL["bf16"]
+
+
 def test_decode_split_counts_agree(gpu):
     import sliding_window_attention_sink_amd as swa
     B, Hq, Hkv, d, s, r, T = 2, 8, 2, 128, 4, 1020, 3000

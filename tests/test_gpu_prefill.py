@@ -139,6 +139,27 @@ def test_large_sink_scores(gpu):
     assert max_err(o, ref) <= TOL["bf16"]
 
 
+def test_score_jump_mid_band(gpu):
+    """Keys that score far above everything before them in the middle of the
+    band (and a second, higher jump later): rows that meet them must raise
+    the running max and rescale O after many tiles at the lower max; rows
+    just past them must fall back to small weights."""
+    B, Hq, Hkv, L, d, s, r = 1, 4, 2, 900, 128, 4, 400
+    g = np.random.default_rng(11)
+    u = g.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = si.round_bf16((g.standard_normal((B, Hq, L, d)) + 2.0 * u).astype(np.float32))
+    k = si.round_bf16(g.standard_normal((B, Hkv, L, d)).astype(np.float32))
+    v = si.round_bf16(g.standard_normal((B, Hkv, L, d)).astype(np.float32))
+    # scores about 2*c/sqrt(d) * |u|^2: +30 for keys 500..505, +60 for 700..703
+    k[:, :, 500:506] = si.round_bf16((u * (15.0 * np.sqrt(d))).astype(np.float32))
+    k[:, :, 700:704] = si.round_bf16((u * (30.0 * np.sqrt(d))).astype(np.float32))
+    say("score jump mid band")
+    o = host(run_prefill(q, k, v, s, r, "bf16"))
+    ref = oracle.prefill_rows(q, k, v, s, r).reshape(o.shape)
+    assert max_err(o, ref) <= TOL["bf16"]
+
+
 def test_deterministic_and_guarded(gpu):
     """Two runs are bit-identical; nothing is written outside the output."""
     import sliding_window_attention_sink_amd as swa
