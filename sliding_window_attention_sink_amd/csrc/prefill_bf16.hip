@@ -538,6 +538,12 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // peeled off the loop.
     int n_last = 0;
     if (nv > 0) {
+        // the queries of tile 0 travel with the first tiles' loads
+        if (wave_active) {
+            const int want_q = (phase_of(0).use_qs && a.qs != a.q) ? 1 : 0;
+            T::load_q(qr, (const __bf16*)(want_q ? a.qs : a.q) + qoff, my_valid, g);
+            q_loaded = want_q;
+        }
         if (grp == 0) {
             issue(K_, 0, 0);
             issue(V_, 0, 1);
