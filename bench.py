@@ -179,11 +179,21 @@ def bench_decode(torch, swa, w, steps=None):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
+    # the streaming generation step with RoPE re-positioning (pre-rotation
+    # cache): more fused steps on the same cache, rope_base 1e4
+    nr = min(256, steps)
+    t0.record(stream)
+    for i in range(nr):
+        swa.decode_step(qd[i], knd[i], vnd[i], kc, vc, w.L + steps + i + 1, w.s, w.r, rope_base=1e4, out=out,
+                        workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_rope = t0.elapsed_time(t1) / nr
     # the decode launch alone: back-to-back launches at the last step's T
     nd = min(64, steps)
     t0.record(stream)
     for i in range(nd):
-        swa.decode(qd[steps - 1], kc, vc, w.L + steps, w.s, w.r, out=out, workspace=ws)
+        swa.decode(qd[steps - 1], kc, vc, w.L + steps + nr, w.s, w.r, out=out, workspace=ws)
     t1.record(stream)
     torch.cuda.synchronize()
     decode_ms = t0.elapsed_time(t1) / nd
@@ -192,7 +202,7 @@ def bench_decode(torch, swa, w, steps=None):
     qo = 2 * w.B * w.Hq * w.d * 2
     app = w.B * w.Hkv * w.d * 2 * 2
     step_bytes = kv + qo + app
-    return {"ms": ms, "ms_separate": ms_separate, "decode_ms": decode_ms, "bytes_per_step": step_bytes, "steps": steps,
+    return {"ms": ms, "ms_separate": ms_separate, "ms_rope": ms_rope, "rope_steps": nr, "decode_ms": decode_ms, "bytes_per_step": step_bytes, "steps": steps,
             "gbs": step_bytes / ms / 1e6, "decode_kernel_bytes": kv + qo}
 
 
@@ -321,6 +331,8 @@ def main():
         dec_gbs = r4["decode_kernel_bytes"] / r4["decode_ms"] / 1e6
         extra[w4.name] = {"GB/s": r4["gbs"], "us_per_step": r4["ms"] * 1e3, "steps": r4["steps"],
                           "us_per_step_separate_append_decode": r4["ms_separate"] * 1e3,
+                          "rope1e4_us_per_step": r4["ms_rope"] * 1e3, "rope1e4_steps": r4["rope_steps"],
+                          "rope1e4_GB/s": r4["bytes_per_step"] / r4["ms_rope"] / 1e6,
                           "bytes_per_step": r4["bytes_per_step"], "frac_hbm_peak": r4["gbs"] / PEAK_HBM_GBS,
                           "decode_launch_us": r4["decode_ms"] * 1e3, "decode_launch_GB/s": dec_gbs,
                           "decode_launch_frac_hbm_peak": dec_gbs / PEAK_HBM_GBS}

@@ -121,9 +121,14 @@ size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split);
  * token first), i.e. U(T-1).  Slot order does not matter to softmax
  * attention over a set, so slots are read in physical order.  Writes
  * o ([B, Hq, d]).  n_split: 0 = the library's choice, else 1 .. 64.
+ * With rope_base > 0 the cache holds keys before rotation and q is given
+ * before rotation; the keys of U(T-1), in temporal order, are rotated to
+ * positions 0 .. |U(T-1)|-1 and the query to |U(T-1)|-1 (the StreamingLLM
+ * re-positioning of swa_prefill with a cache; pair j with j + d/2, angle
+ * position * rope_base^(-2j/d)).
  * Errors: SWA_ERR_INVALID_ARG (null/misaligned pointer, T < 1, workspace too
  * small, n_split out of range), SWA_ERR_UNSUPPORTED (d, dtype other than
- * bf16, RoPE), SWA_ERR_HIP.
+ * bf16), SWA_ERR_HIP.
  */
 int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const void* v_cache, int64_t T,
                void* o, int32_t n_split, void* workspace, size_t workspace_bytes, void* stream);

@@ -22,6 +22,14 @@
 //    and split; a second kernel merges the splits and normalises.  With one
 //    split (enough (batch, kv-head) units to fill the chip) the workgroup
 //    writes the normalised output itself and the second kernel is skipped.
+//  * RoPE re-positioning (rope_log2_base > 0): the cache holds keys before
+//    rotation and U(T-1) sits at consecutive positions in temporal order, the
+//    query at the last (the StreamingLLM paragraph after
+//    eq:attn-fixed-streaming on the t6page page): the query is rotated once
+//    to min(T-1, s+r-1) and every key, as it arrives in registers, to its
+//    rank (sinks j -> j; a window token p -> s + p - max(s, T-r)).  Angles
+//    are reduced in fp64, then turned by v_sin/v_cos in fp32; dimension j
+//    pairs with j + d/2 and turns by rank * base^(-2j/d).
 //  * fused step (kn/vn given): the workgroup whose slot range holds the
 //    current token's slot first writes the token's K/V row there (then
 //    waits for the stores and a barrier), so one launch does the append and
@@ -59,6 +67,29 @@ struct DecodeSmem {
 };
 
 __device__ __forceinline__ int vswz(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
+
+// Rotate the eight dimension pairs (lo[e], hi[e]) (dims j and j + d/2, bf16)
+// by pos * fr[e] revolutions.
+__device__ __forceinline__ void rope_rot8(u32x4& lo, u32x4& hi, const double* fr, double pos) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t rl = 0, rh = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const double rv = pos * fr[2 * w + h];
+            const float x = (float)(rv - __builtin_floor(rv));
+            const float c = __builtin_amdgcn_cosf(x), sn = __builtin_amdgcn_sinf(x);
+            const float x0 = __builtin_bit_cast(float, (lo[w] >> (16 * h)) << 16);
+            const float x1 = __builtin_bit_cast(float, (hi[w] >> (16 * h)) << 16);
+            const uint32_t y0 = __builtin_bit_cast(uint16_t, (__bf16)(x0 * c - x1 * sn));
+            const uint32_t y1 = __builtin_bit_cast(uint16_t, (__bf16)(x0 * sn + x1 * c));
+            rl |= y0 << (16 * h);
+            rh |= y1 << (16 * h);
+        }
+        lo[w] = rl;
+        hi[w] = rh;
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
@@ -112,16 +143,43 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
         return first <= T - 1;
     };
 
+    // RoPE: revolutions per position of this lane's first-half dims
+    // 32 ks + 8 g + e (ks < HK); the partner dims sit at k-step ks + HK
+    constexpr int HK = KSTEPS / 2;
+    const bool rope = a.rope_log2_base > 0.0;
+    double frev[HK * 8];
+    if (rope) {
+#pragma unroll
+        for (int ks = 0; ks < HK; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                frev[8 * ks + e] = exp2(-(2.0 * (32 * ks + 8 * g + e) / D) * a.rope_log2_base) * 0.15915494309189535;
+    }
+    // position of the key in slot j among U(T-1) in temporal order
+    const int64_t win_lo = (T - a.r) > a.s ? (T - a.r) : (int64_t)a.s;
+    auto rank_of = [&](int j) -> double {
+        if (j < a.s) return (double)j;
+        const uint32_t q = (uint32_t)(j - a.s);
+        const int64_t p = (T - 1) - (int64_t)(((uint32_t)(T - 1) - q) % (uint32_t)a.r);
+        return (double)(a.s + p - win_lo);
+    };
+
     // Q^T operand: column col = head kvh*G + col (zero past the group)
     bf16x8 qreg[KSTEPS];
     {
         const bool qv = col < G;
         const __bf16* qrow = (const __bf16*)a.q + ((size_t)b * a.Hq + kvh * G + (qv ? col : 0)) * D;
+        u32x4 x[KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            u32x4 x = qv ? *(const u32x4*)(qrow + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
-            qreg[ks] = __builtin_bit_cast(bf16x8, x);
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            x[ks] = qv ? *(const u32x4*)(qrow + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+        if (rope) {
+            const double qpos = (double)(T - 1 < (int64_t)S - 1 ? T - 1 : (int64_t)S - 1);
+#pragma unroll
+            for (int ks = 0; ks < HK; ++ks) rope_rot8(x[ks], x[ks + HK], frev + 8 * ks, qpos);
         }
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, x[ks]);
     }
 
     f32x4 oacc[DB];
@@ -151,6 +209,14 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     if (st0 < st1) load(st0);
     for (int st = st0; st < st1; ++st) {
         const int kb = j0 + st * KW;
+        if (rope) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const double pos = rank_of(kb + dec_key(bb, col));
+#pragma unroll
+                for (int ks = 0; ks < HK; ++ks) rope_rot8(kr[bb][ks], kr[bb][ks + HK], frev + 8 * ks, pos);
+            }
+        }
         f32x4 sacc[2];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {

@@ -273,7 +273,6 @@ int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void*
     int st = check_desc(desc, fn);
     if (st) return st;
     if (desc->dtype != SWA_BF16) return fail(SWA_ERR_UNSUPPORTED, "%s: decode is built for bf16 only", fn);
-    if (desc->rope_base > 0.0f) return fail(SWA_ERR_UNSUPPORTED, "%s: decode with RoPE is not built", fn);
     if (desc->Hq / desc->Hkv > 16)
         return fail(SWA_ERR_UNSUPPORTED, "%s: more than 16 q-heads per kv-head", fn);
     if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k_cache, fn, "k_cache")) ||
@@ -312,6 +311,7 @@ int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void*
     a.n_split = n_split;
     a.slots_per_split = sps;
     a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
+    a.rope_log2_base = desc->rope_base > 0.0f ? std::log2((double)desc->rope_base) : 0.0;
     return hip_status(swa::launch_decode_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 

@@ -53,6 +53,7 @@ struct DecodeArgs {
     const void* vn;     // same for V
     int64_t T;          // tokens in the cache including the current one
     int32_t j_new;      // cache slot of token T-1 with kn/vn, else -1
+    double rope_log2_base;  // log2(RoPE base), 0 = no RoPE
     int32_t B, Hq, Hkv, s, r;
     int32_t n_split;
     int32_t slots_per_split;

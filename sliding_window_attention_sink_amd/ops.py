@@ -100,12 +100,14 @@ def decode_workspace_bytes(desc: SwaDesc, n_split: int = 0) -> int:
     return _lib.swa_decode_workspace_bytes(desc, n_split)
 
 
-def decode(q, k_cache, v_cache, T, s, r, *, scale=None, n_split=0, out=None, workspace=None, stream=None):
-    """Decode step: q [B,Hq,d] of token T-1 over the cache holding tokens 0..T-1."""
+def decode(q, k_cache, v_cache, T, s, r, *, scale=None, rope_base=0.0, n_split=0, out=None, workspace=None,
+           stream=None):
+    """Decode step: q [B,Hq,d] of token T-1 over the cache holding tokens 0..T-1
+    (rope_base > 0: pre-rotation q and keys, StreamingLLM re-positioning)."""
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     dev = q.device
-    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale)
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale, rope_base=rope_base)
     _need(k_cache, "k_cache", (B, Hkv, s + r, d), q.dtype, dev)
     _need(v_cache, "v_cache", (B, Hkv, s + r, d), q.dtype, dev)
     if out is None:
@@ -119,13 +121,13 @@ def decode(q, k_cache, v_cache, T, s, r, *, scale=None, n_split=0, out=None, wor
     return out
 
 
-def decode_step(q, k_new, v_new, k_cache, v_cache, T, s, r, *, scale=None, n_split=0, out=None, workspace=None,
-                stream=None):
+def decode_step(q, k_new, v_new, k_cache, v_cache, T, s, r, *, scale=None, rope_base=0.0, n_split=0, out=None,
+                workspace=None, stream=None):
     """Append token T-1 (k_new/v_new [B,Hkv,d]) and decode its query q [B,Hq,d], in one launch."""
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     dev = q.device
-    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale)
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale, rope_base=rope_base)
     _need(k_new, "k_new", (B, Hkv, d), q.dtype, dev)
     _need(v_new, "v_new", (B, Hkv, d), q.dtype, dev)
     _need(k_cache, "k_cache", (B, Hkv, s + r, d), q.dtype, dev)

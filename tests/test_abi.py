@@ -122,7 +122,6 @@ def test_decode_rejects():
     assert dec(wsb=ws - 4) == -1 and "workspace" in _lib.swa_last_error()
     assert dec(q=None) == -1
     assert dec(dd=desc(dtype=_lib.SWA_F32)) == -2
-    assert dec(dd=desc(rope_base=1e4)) == -2
     assert dec(dd=desc(Hq=34, Hkv=2)) == -2 and "16 q-heads" in _lib.swa_last_error()
 
 

@@ -114,6 +114,64 @@ def test_decode_step_equals_append_then_decode(gpu, B, Hq, Hkv, d, s, r, n_split
     assert max_err(host(o2), ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,d,s,r,n_split,base", [
+    (1, 8, 2, 128, 4, 60, 0, 1e4),
+    (2, 4, 4, 64, 3, 45, 3, 500.0),
+    (1, 2, 1, 128, 70, 30, 1, 1e4),
+])
+def test_decode_rope_matches_oracle(gpu, B, Hq, Hkv, d, s, r, n_split, base):
+    """RoPE re-positioning on the pre-rotation cache (the streaming
+    generation step): T = 1 .. 2(s+r)+20 through sink, filling and wrapped
+    slots, fused and unfused steps, against the fp64 row definition."""
+    import sliding_window_attention_sink_amd as swa
+    steps = 2 * (s + r) + 20
+    g = np.random.default_rng(B * 77 + Hq + d + s + r)
+    K = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    V = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    Q = si.round_bf16(g.standard_normal((B, Hq, steps, d)).astype(np.float32))
+    kc1, vc1 = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    kc2, vc2 = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    Kd, Vd, Qd = dev(K, "bf16"), dev(V, "bf16"), dev(Q, "bf16")
+    o1 = torch.empty((steps, B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    say("decode rope", B, Hq, Hkv, d, s, r, n_split, base)
+    for t in range(steps):
+        kt, vt, qt = Kd[:, :, t].contiguous(), Vd[:, :, t].contiguous(), Qd[:, :, t].contiguous()
+        swa.cache_append(kt.unsqueeze(2), vt.unsqueeze(2), kc1, vc1, t, s, r)
+        swa.decode(qt, kc1, vc1, t + 1, s, r, rope_base=base, n_split=n_split, out=o1[t])
+        swa.decode_step(qt, kt, vt, kc2, vc2, t + 1, s, r, rope_base=base, n_split=n_split, out=o2[t])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2))
+    rows = np.array([[b, h, t] for t in range(steps) for b in range(B) for h in range(Hq)])
+    ref = oracle.prefill_rows(Q, K, V, s, r, rope_base=base, rows=rows).reshape(steps, B, Hq, d)
+    assert max_err(host(o1), ref) <= TOL["bf16"]
+
+
+def test_decode_rope_equals_one_token_chunks(gpu):
+    """Decode with RoPE is chunked prefill with chunk 1: the two kernels
+    agree on every step of a run past the wrap."""
+    import sliding_window_attention_sink_amd as swa
+    B, Hq, Hkv, d, s, r, base = 1, 4, 2, 128, 4, 100, 1e4
+    steps = 300
+    g = np.random.default_rng(3)
+    K = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    V = si.round_bf16(g.standard_normal((B, Hkv, steps, d)).astype(np.float32))
+    Q = si.round_bf16(g.standard_normal((B, Hq, steps, d)).astype(np.float32))
+    kc, vc = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
+    Kd, Vd, Qd = dev(K, "bf16"), dev(V, "bf16"), dev(Q, "bf16")
+    say("decode rope vs chunk 1")
+    worst = 0.0
+    for t in range(steps):
+        kt, vt = Kd[:, :, t:t + 1].contiguous(), Vd[:, :, t:t + 1].contiguous()
+        qt = Qd[:, :, t:t + 1].contiguous()
+        op = swa.prefill(qt, kt, vt, s, r, rope_base=base, k_cache=kc if t else None, v_cache=vc if t else None,
+                         pos0=t)
+        swa.cache_append(kt, vt, kc, vc, t, s, r)
+        od = swa.decode(qt[:, :, 0].contiguous(), kc, vc, t + 1, s, r, rope_base=base)
+        worst = max(worst, max_err(host(od), host(op[:, :, 0]).astype(np.float64)))
+    assert worst <= TOL["bf16"], worst
+
+
 def test_decode_split_counts_agree(gpu):
     import sliding_window_attention_sink_amd as swa
     B, Hq, Hkv, d, s, r, T = 2, 8, 2, 128, 4, 1020, 3000
