@@ -130,6 +130,33 @@ def bench_prefill(torch, swa, w, steps, warmup):
     return {"ms": ms, "kernel_ms": ms, "flops": flops, "tflops": flops / ms / 1e9}
 
 
+def bench_window_sweep(torch, swa, w, windows, steps=10):
+    """Prefill of the main workload's tensors at several window sizes r (s as
+    given), up to r >= L, i.e. full causal attention: time and cache size."""
+    q, k, v = __import__("swa_inputs").prefill_inputs(w)
+    qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
+    del q, k, v
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for r in windows:
+        for _ in range(2):
+            swa.prefill(qd, kd, vd, w.s, r, out=out)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            swa.prefill(qd, kd, vd, w.s, r, out=out)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        flops = 4.0 * w.d * key_count_sum(w.L, w.s, r) * w.B * w.Hq
+        res["r%d" % r] = {"ms": ms, "tflops": flops / ms / 1e9,
+                          "cache_slots": min(w.s + r, w.L), "full_attention": w.s + r >= w.L}
+    return res
+
+
 def bench_decode(torch, swa, w, steps=None):
     si = __import__("swa_inputs")
     steps = w.steps if steps is None else steps
@@ -279,8 +306,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time the main workload only")
-    ap.add_argument("--extra", default="3,4,5,1",
-                    help="other workloads to time alongside (comma list of 1,3,4,5 or 'none')")
+    ap.add_argument("--extra", default="3,4,5,6,1",
+                    help="other workloads to time alongside (comma list of 1,3,4,5, 6 = window sweep of the "
+                         "main workload, or 'none')")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's 1024)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -344,6 +372,10 @@ def main():
         extra[w5.name] = {"tflops": r5["tflops"], "ms": r5["ms"], "frac_bf16_peak": r5["tflops"] / PEAK_BF16_TFLOPS,
                           "prefill_call_ms": r5["prefill_call_ms"]}
         log("w5", r5)
+        torch.cuda.empty_cache()
+    if 6 in todo:
+        # window sweep on the main workload's tensors, to the full-attention limit
+        extra["window_sweep_" + w.name] = bench_window_sweep(torch, swa, w, [512, 1024, 2048, 4096, 8192])
         torch.cuda.empty_cache()
     if 1 in todo:
         w1 = si.WORKLOADS[1]
