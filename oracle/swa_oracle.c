@@ -15,6 +15,11 @@
  *    always-visible first s = 4 tokens next to the window); the
  *    eq:attn-fixed-streaming cache composition (sinks KV[0:k] plus recent
  *    KV[t-m:t]) on the t6page "滑窗与固定稀疏" page.
+ *    With a dilation delta >= 1 the window keeps r keys but takes every
+ *    delta-th position, t, t - delta, ..., t - (r-1) delta (the glossary
+ *    entry on dilated SWA and the Longformer section of that page: attended
+ *    positions skip delta - 1 tokens, same count, wider reach); the sinks
+ *    are unchanged and a key in both sets counts once.  delta = 1 is U(t).
  *
  *  - Scores and normalisation.  x_i = (q_t . k_i) / sqrt(d) (here: times the
  *    caller's scale), then softmax over U(t) and the weighted sum of values:
@@ -45,14 +50,15 @@
 
 /* Number of keys in U(t) and the list itself, sinks first, then the window,
  * which together are in increasing (temporal) order. */
-static int64_t key_set(int64_t t, int64_t s, int64_t r, int64_t* keys) {
+static int64_t key_set(int64_t t, int64_t s, int64_t r, int64_t dil, int64_t* keys) {
     int64_t n = 0;
     int64_t ns = s < t + 1 ? s : t + 1;
     for (int64_t j = 0; j < ns; ++j) keys[n++] = j;
-    int64_t lo = t - r + 1;
-    if (lo < s) lo = s;
-    if (lo < 0) lo = 0;
-    for (int64_t i = lo; i <= t; ++i) keys[n++] = i;
+    /* window positions t - dil*m, m = r-1 .. 0 (increasing), those >= s */
+    for (int64_t m = r - 1; m >= 0; --m) {
+        int64_t i = t - dil * m;
+        if (i >= s && i >= 0) keys[n++] = i;
+    }
     return n;
 }
 
@@ -103,9 +109,10 @@ static void rope_rotate(const rope_table* T, const double* x, double* y, int64_t
 int swa_oracle_rows(const float* q, const float* k, const float* v,
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d,
                     int64_t s, int64_t r, double scale, double rope_base, int64_t qpos0,
-                    int64_t nrows, const int64_t* rows, double* out, int64_t* nkeys) {
+                    int64_t nrows, const int64_t* rows, double* out, int64_t* nkeys, int64_t dil) {
     if (!q || !k || !v || !rows || !out) return ORACLE_EINVAL;
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || r < 1 || s < 0 || qpos0 < 0) return ORACLE_EINVAL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || r < 1 || s < 0 || qpos0 < 0 || dil < 1)
+        return ORACLE_EINVAL;
     if (rope_base > 0 && (d % 2)) return ORACLE_EINVAL;
     for (int64_t n = 0; n < nrows; ++n) {
         int64_t b = rows[3 * n], h = rows[3 * n + 1], i = rows[3 * n + 2];
@@ -139,7 +146,7 @@ int swa_oracle_rows(const float* q, const float* k, const float* v,
                 const float* kbase = k + (b * Hkv + kvh) * Lk * d;
                 const float* vbase = v + (b * Hkv + kvh) * Lk * d;
 
-                int64_t nk = key_set(t, s, r, keys);
+                int64_t nk = key_set(t, s, r, dil, keys);
                 if (nkeys) nkeys[n] = nk;
 
                 for (int64_t e = 0; e < d; ++e) qd[e] = (double)qrow[e];
@@ -219,9 +226,9 @@ int swa_oracle_rope(const double* x, double* y, int64_t d, int64_t pos, double b
 }
 
 /* |U(t)| and the key list, exposed for the key-set pins. */
-int64_t swa_oracle_key_set(int64_t t, int64_t s, int64_t r, int64_t* keys) {
-    if (t < 0 || s < 0 || r < 1 || !keys) return ORACLE_EINVAL;
-    return key_set(t, s, r, keys);
+int64_t swa_oracle_key_set(int64_t t, int64_t s, int64_t r, int64_t dil, int64_t* keys) {
+    if (t < 0 || s < 0 || r < 1 || dil < 1 || !keys) return ORACLE_EINVAL;
+    return key_set(t, s, r, dil, keys);
 }
 
 /* Threads the parallel loops use (the CPU-baseline leg reports it). */

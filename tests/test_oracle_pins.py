@@ -361,3 +361,54 @@ def test_rope_full_cache_ignores_absolute_position():
     w = np.exp(x - x.max())
     true_pos = (w / w.sum()) @ vv[idx].astype(np.float64)
     assert np.abs(true_pos - outs[2]).max() > 1e-3
+
+
+# ---- dilated window (glossary entry on dilated SWA and the Longformer
+# section of the t6page page: attended positions skip delta-1 tokens; the
+# count of window keys, r, is unchanged)
+
+def _dilated_set(t, s, r, dil):
+    """The definition, written as a set: sinks up to t, then r positions back
+    from t in steps of dil, each key once."""
+    return sorted({i for i in range(t + 1) if i < s} | {t - dil * m for m in range(r) if t - dil * m >= 0})
+
+
+@pytest.mark.parametrize("s,r,dil", [(0, 1, 3), (0, 4, 2), (2, 3, 3), (4, 5, 4), (3, 2, 7), (1, 6, 1)])
+def test_dilated_key_set_brute_force(s, r, dil):
+    for t in range(0, 40):
+        assert list(oracle.key_set(t, s, r, dil)) == _dilated_set(t, s, r, dil), (t, s, r, dil)
+
+
+@pytest.mark.parametrize("s,r,dil", [(0, 4, 2), (4, 3, 5), (2, 10, 3)])
+def test_dilated_key_count_closed_form(s, r, dil):
+    # |U| = min(s, t+1) + (t >= s ? min(r, floor((t - s) / dil) + 1) : 0)
+    for t in range(0, 60):
+        win = min(r, (t - s) // dil + 1) if t >= s else 0
+        assert len(oracle.key_set(t, s, r, dil)) == min(s, t + 1) + win
+
+
+def test_dilated_rows_equal_attention_over_explicit_sets():
+    """Rows with a dilation equal softmax attention over the key set written
+    out by hand (attend_set: a separate routine of the oracle)."""
+    g = np.random.default_rng(21)
+    B, Hq, Hkv, L, d, s, r, dil = 1, 4, 2, 50, 16, 3, 5, 4
+    q = g.standard_normal((B, Hq, L, d)).astype(np.float32)
+    k = g.standard_normal((B, Hkv, L, d)).astype(np.float32)
+    v = g.standard_normal((B, Hkv, L, d)).astype(np.float32)
+    got = oracle.prefill_rows(q, k, v, s, r, dilation=dil).reshape(B, Hq, L, d)
+    for h in range(Hq):
+        kvh = h // (Hq // Hkv)
+        for t in range(L):
+            keys = _dilated_set(t, s, r, dil)
+            want = oracle.attend_set(q[0, h, t], k[0, kvh, keys], v[0, kvh, keys])
+            assert np.abs(got[0, h, t] - want).max() < 1e-12, (h, t)
+
+
+def test_dilation_one_is_the_plain_window():
+    g = np.random.default_rng(22)
+    q = g.standard_normal((1, 2, 40, 8)).astype(np.float32)
+    k = g.standard_normal((1, 2, 40, 8)).astype(np.float32)
+    v = g.standard_normal((1, 2, 40, 8)).astype(np.float32)
+    a = oracle.prefill_rows(q, k, v, 2, 7)
+    b = oracle.prefill_rows(q, k, v, 2, 7, dilation=1)
+    assert np.array_equal(a, b)
