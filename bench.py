@@ -157,6 +157,44 @@ def bench_window_sweep(torch, swa, w, windows, steps=10):
     return res
 
 
+def dilated_key_count_sum(L: int, s: int, r: int, dil: int) -> int:
+    """sum over rows t of |U(t)| with a dilated window: min(s, t+1) sinks plus
+    min(r, (t-s)//dil + 1) window keys for t >= s."""
+    t = np.arange(L, dtype=np.int64)
+    win = np.where(t >= s, np.minimum(r, (t - s) // dil + 1), 0)
+    return int((np.minimum(s, t + 1) + win).sum())
+
+
+def bench_dilated(torch, swa, w, dilations, steps=10):
+    """Dilated-window prefill of the main workload's tensors (gather, banded
+    prefill of the residue classes, scatter), algorithmic TFLOP/s."""
+    q, k, v = __import__("swa_inputs").prefill_inputs(w)
+    qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
+    del q, k, v
+    out = torch.empty_like(qd)
+    desc = swa.make_desc(w.B, w.Hq, w.Hkv, w.d, w.s, w.r, torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for dil in dilations:
+        ws = torch.empty(max(16, swa._lib.swa_prefill_dilated_workspace_bytes(desc, w.L, dil)), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(2):
+            swa.prefill_dilated(qd, kd, vd, w.s, w.r, dil, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(steps):
+            swa.prefill_dilated(qd, kd, vd, w.s, w.r, dil, out=out, workspace=ws)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        flops = 4.0 * w.d * dilated_key_count_sum(w.L, w.s, w.r, dil) * w.B * w.Hq
+        res["dilation%d" % dil] = {"ms": ms, "tflops": flops / ms / 1e9, "reach": w.s + dil * (w.r - 1) + 1}
+        del ws
+    return res
+
+
 def bench_decode(torch, swa, w, steps=None):
     si = __import__("swa_inputs")
     steps = w.steps if steps is None else steps
@@ -306,9 +344,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time the main workload only")
-    ap.add_argument("--extra", default="3,4,5,6,1",
+    ap.add_argument("--extra", default="3,4,5,6,7,1",
                     help="other workloads to time alongside (comma list of 1,3,4,5, 6 = window sweep of the "
-                         "main workload, or 'none')")
+                         "main workload, 7 = its dilated-window prefill, or 'none')")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's 1024)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -376,6 +414,9 @@ def main():
     if 6 in todo:
         # window sweep on the main workload's tensors, to the full-attention limit
         extra["window_sweep_" + w.name] = bench_window_sweep(torch, swa, w, [512, 1024, 2048, 4096, 8192])
+        torch.cuda.empty_cache()
+    if 7 in todo:
+        extra["dilated_" + w.name] = bench_dilated(torch, swa, w, [2, 4])
         torch.cuda.empty_cache()
     if 1 in todo:
         w1 = si.WORKLOADS[1]

@@ -108,6 +108,24 @@ int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new,
                      void* k_cache, void* v_cache, void* stream);
 
 /*
+ * Dilated sliding window (prefill, no cache, no RoPE): query t attends the
+ * sinks 0 .. min(s, t+1)-1 and the r positions t, t - dilation, ...,
+ * t - (r-1) dilation that are >= s (the glossary entry on dilated SWA and
+ * the Longformer section of the t6page page "滑窗与固定稀疏": attended
+ * positions skip dilation-1 tokens, the number of keys is unchanged).
+ * Layouts as for swa_prefill.  dilation = 1 is swa_prefill without a cache.
+ * Otherwise the positions of each residue class mod dilation (after the
+ * sink rows) are gathered into a workspace of
+ * swa_prefill_dilated_workspace_bytes() bytes, attended as an ordinary
+ * window and scattered back.  Errors: those of swa_prefill, and
+ * SWA_ERR_INVALID_ARG for dilation < 1 or a short/NULL workspace,
+ * SWA_ERR_UNSUPPORTED with RoPE.
+ */
+size_t swa_prefill_dilated_workspace_bytes(const swa_desc* desc, int64_t L, int32_t dilation);
+int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, const void* k, const void* v, void* o,
+                        int64_t L, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-K decode.  Bytes of workspace swa_decode needs for n_split splits of
  * the s + r slots (0 = the library's choice for this shape):
  * B * Hq * n_split * (d + 2) * 4 bytes, or 0 for one split (the split

@@ -5,6 +5,7 @@ of include/swa.h); this package binds it for PyTorch callers:
 
   * prefill(q, k, v, s, r, ...)        banded flash-style prefill, optional
                                        rolling cache (chunked) and RoPE
+  * prefill_dilated(q, k, v, s, r, dilation) the same with a dilated window
   * cache_append(k, v, kc, vc, pos0, ...) write tokens into the rolling cache
   * decode(q, kc, vc, T, s, r, ...)    split-K single-query decode
   * decode_step(q, k, v, kc, vc, T, s, r, ...) append token T-1 and decode
@@ -21,5 +22,6 @@ from .ops import (  # noqa: F401
     make_desc,
     new_cache,
     prefill,
+    prefill_dilated,
     prefill_workspace_bytes,
 )

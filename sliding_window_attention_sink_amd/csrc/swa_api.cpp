@@ -101,6 +101,29 @@ int32_t default_splits(const swa_desc* d) {
     return (int32_t)n;
 }
 
+// Residue-class layout of a dilated prefill: every class sequence holds the
+// s1 = min(s, L) sink rows and then its positions >= s1 (at most
+// ceil((L - s1) / dil) of them); Q, K, V and O copies of that shape.
+struct DilateLayout {
+    int64_t s1 = 0, Lc = 0;
+    size_t q = 0, k = 0, v = 0, o = 0, total = 0;
+};
+
+DilateLayout dilate_layout(const swa_desc* d, int64_t L, int64_t dil) {
+    DilateLayout x;
+    x.s1 = d->s < L ? d->s : L;
+    x.Lc = x.s1 + (L - x.s1 + dil - 1) / dil;
+    const size_t rb = (size_t)d->d * elem_bytes(d);
+    const size_t qn = round_up((size_t)d->B * dil * d->Hq * x.Lc * rb, 256);
+    const size_t kn = round_up((size_t)d->B * dil * d->Hkv * x.Lc * rb, 256);
+    x.q = 0;
+    x.k = qn;
+    x.v = qn + kn;
+    x.o = qn + 2 * kn;
+    x.total = 2 * qn + 2 * kn;
+    return x;
+}
+
 // Per-split partial results (max, sum, unnormalised O) per query head; one
 // split writes the output directly and needs none.
 size_t decode_ws_bytes(const swa_desc* desc, int32_t n_split) {
@@ -247,6 +270,53 @@ int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new,
     a.d = desc->d;
     a.elem_bytes = (int32_t)elem_bytes(desc);
     return hip_status(swa::launch_append(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t swa_prefill_dilated_workspace_bytes(const swa_desc* desc, int64_t L, int32_t dilation) {
+    if (check_desc(desc, "swa_prefill_dilated_workspace_bytes") != SWA_OK || L < 1 || dilation < 1) return 0;
+    if (dilation == 1 || desc->rope_base > 0.0f) return 0;
+    return dilate_layout(desc, L, dilation).total;
+}
+
+int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, const void* k, const void* v, void* o,
+                        int64_t L, void* workspace, size_t workspace_bytes, void* stream) {
+    static const char* fn = "swa_prefill_dilated";
+    clear_error();
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    if (dilation < 1) return fail(SWA_ERR_INVALID_ARG, "%s: dilation must be >= 1 (got %d)", fn, dilation);
+    if (desc->rope_base > 0.0f) return fail(SWA_ERR_UNSUPPORTED, "%s: dilation with RoPE is not built", fn);
+    if (dilation == 1) return swa_prefill(desc, q, k, v, o, L, nullptr, nullptr, 0, workspace, workspace_bytes, stream);
+    if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k, fn, "k")) || (st = check_ptr(v, fn, "v")) ||
+        (st = check_ptr(o, fn, "o")) || (st = check_ptr(workspace, fn, "workspace")))
+        return st;
+    if (L < 1) return fail(SWA_ERR_INVALID_ARG, "%s: L must be >= 1 (got %lld)", fn, (long long)L);
+    if (L > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
+    if ((int64_t)desc->B * dilation > 0x7fffffffLL) return fail(SWA_ERR_INVALID_ARG, "%s: B * dilation too large", fn);
+    const DilateLayout lay = dilate_layout(desc, L, dilation);
+    if (workspace_bytes < lay.total)
+        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    swa::DilateArgs da{};
+    da.L = L;
+    da.Lc = lay.Lc;
+    da.s1 = lay.s1;
+    da.dil = dilation;
+    da.B = desc->B;
+    da.row_bytes = (int32_t)(desc->d * elem_bytes(desc));
+    if ((st = hip_status(swa::launch_dilate_gather(da, q, ws + lay.q, desc->Hq, hs), fn)) ||
+        (st = hip_status(swa::launch_dilate_gather(da, k, ws + lay.k, desc->Hkv, hs), fn)) ||
+        (st = hip_status(swa::launch_dilate_gather(da, v, ws + lay.v, desc->Hkv, hs), fn)))
+        return st;
+    // the classes are extra batch entries of an ordinary prefill
+    swa_desc cd = *desc;
+    cd.B = (int32_t)(desc->B * dilation);
+    if ((st = swa_prefill(&cd, ws + lay.q, ws + lay.k, ws + lay.v, ws + lay.o, lay.Lc, nullptr, nullptr, 0, nullptr,
+                          0, stream)))
+        return st;
+    return hip_status(swa::launch_dilate_scatter(da, ws + lay.o, o, desc->Hq, hs), fn);
 }
 
 int32_t swa_decode_default_splits(const swa_desc* desc) {

@@ -80,6 +80,16 @@ int prefill_bf16_rows_per_block(int Hq, int Hkv);
 // Launchers (return hipError_t of the launch).  `d` selects the instantiation.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, hipStream_t st);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
+// Dilated window: residue-class sequences [B * dil, H, Lc, row_bytes] <->
+// positions [B, H, L, row_bytes]; s1 = min(s, L) sink rows lead every class.
+struct DilateArgs {
+    int64_t L, Lc, s1, dil;
+    int32_t B;
+    int32_t row_bytes;   // d * element size, a multiple of 16
+};
+
+hipError_t launch_dilate_gather(const DilateArgs& a, const void* src, void* dst, int32_t H, hipStream_t st);
+hipError_t launch_dilate_scatter(const DilateArgs& a, const void* src, void* dst, int32_t H, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t st);
 hipError_t launch_rope_prepare_bf16(const RopeArgs& a, int d, hipStream_t st);

@@ -84,6 +84,25 @@ def new_cache(B, Hkv, d, s, r, dtype, device, fill=0.0):
     return kc, vc
 
 
+def prefill_dilated(q, k, v, s, r, dilation, *, scale=None, out=None, workspace=None, stream=None):
+    """Prefill with a dilated window: row t attends the sinks and t, t-dilation, ..., t-(r-1)dilation."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale)
+    _need(k, "k", (B, Hkv, L, d), q.dtype, dev)
+    _need(v, "v", (B, Hkv, L, d), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.shape, q.dtype, dev)
+    wsb = _lib.swa_prefill_dilated_workspace_bytes(desc, L, dilation)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    check(_lib.swa_prefill_dilated(desc, dilation, _ptr(q), _ptr(k), _ptr(v), _ptr(out), L, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), _stream(dev, stream)))
+    return out
+
+
 def cache_append(k_new, v_new, k_cache, v_cache, pos0, s, r, *, stream=None):
     """Write tokens pos0 .. pos0+n-1 (k_new/v_new [B,Hkv,n,d]) into the rolling cache."""
     B, Hkv, n, d = k_new.shape

@@ -139,6 +139,22 @@ def test_decode_step_rejects():
     assert step(wsb=ws - 4) == -1 and "workspace" in _lib.swa_last_error()
 
 
+def test_prefill_dilated_rejects():
+    d_ = desc()
+    wsb = _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 3)
+    assert wsb > 0 and _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 1) == 0
+    assert _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 0) == 0
+
+    def dil(dd=d_, dl=3, ws=W, n=wsb, L=100):
+        return _lib.swa_prefill_dilated(dd, dl, A, B_, C, D, L, ws, n, None)
+
+    assert dil(dl=0) == -1 and "dilation" in _lib.swa_last_error()
+    assert dil(dd=desc(rope_base=1e4)) == -2
+    assert dil(ws=None) == -1 and "workspace" in _lib.swa_last_error()
+    assert dil(n=wsb - 16) == -1 and "workspace" in _lib.swa_last_error()
+    assert dil(L=0) == -1
+
+
 def test_last_error_is_per_call():
     assert prefill(desc(r=0)) == -1
     assert _lib.swa_last_error() != ""

@@ -160,6 +160,40 @@ def test_score_jump_mid_band(gpu):
     assert max_err(o, ref) <= TOL["bf16"]
 
 
+# (case, dtype, B, Hq, Hkv, d, L, s, r, dilation): residue classes of unequal
+# length, sinks past the first tile, dilation beyond the window and beyond L
+DILATED = [
+    (60, "bf16", 1, 4, 2, 128, 700, 4, 60, 3),
+    (61, "bf16", 2, 2, 2, 64, 333, 0, 40, 2),
+    (62, "bf16", 1, 2, 1, 128, 500, 70, 20, 7),
+    (63, "f32", 1, 2, 2, 64, 257, 4, 28, 4),
+    (64, "bf16", 1, 2, 2, 128, 90, 4, 8, 100),
+]
+
+
+@pytest.mark.parametrize("case", DILATED, ids=[f"dil{c[0]}_{c[1]}_L{c[6]}_d{c[9]}" for c in DILATED])
+def test_dilated_prefill_matches_oracle(gpu, case):
+    import sliding_window_attention_sink_amd as swa
+    cid, dtype, B, Hq, Hkv, d, L, s, r, dil = case
+    q, k, v = case_inputs(cid, B, Hq, Hkv, L, d, dtype)
+    say("dilated prefill", case)
+    o = swa.prefill_dilated(dev(q, dtype), dev(k, dtype), dev(v, dtype), s, r, dil)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_rows(q, k, v, s, r, dilation=dil).reshape(B, Hq, L, d)
+    assert max_err(host(o), ref) <= TOL[dtype]
+
+
+def test_dilation_one_is_plain_prefill(gpu):
+    import sliding_window_attention_sink_amd as swa
+    q, k, v = case_inputs(65, 1, 4, 2, 400, 128, "bf16")
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    say("dilation 1")
+    a = swa.prefill(qd, kd, vd, 4, 50)
+    b = swa.prefill_dilated(qd, kd, vd, 4, 50, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b))
+
+
 def test_deterministic_and_guarded(gpu):
     """Two runs are bit-identical; nothing is written outside the output."""
     import sliding_window_attention_sink_amd as swa
