@@ -91,7 +91,7 @@ __device__ __forceinline__ void rope_rot8(u32x4& lo, u32x4& hi, const double* fr
     }
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     __shared__ DecodeSmem<D> sm;
     constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     // RoPE: revolutions per position of this lane's first-half dims
     // 32 ks + 8 g + e (ks < HK); the partner dims sit at k-step ks + HK
     constexpr int HK = KSTEPS / 2;
-    const bool rope = a.rope_log2_base > 0.0;
+    constexpr bool rope = ROPE;
     double frev[HK * 8];
     if (rope) {
 #pragma unroll
@@ -188,8 +188,14 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     float m_c = -__builtin_inff(), l_part = 0.0f;
     const float c = a.scale_log2e;
 
-    u32x4 kr[2][KSTEPS], vr[KPL];
-    auto load = [&](int st) {
+    // one step's K (MFMA operand order) and V rows in registers; without
+    // RoPE two such buffers keep two steps of loads in flight per wave
+    struct StepRegs {
+        u32x4 k[2][KSTEPS];
+        u32x4 v[KPL];
+    };
+    constexpr int DEPTH = ROPE ? 1 : 2;
+    auto load = [&](StepRegs& R, int st) __attribute__((always_inline)) {
         const int kb = j0 + st * KW;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
@@ -197,17 +203,18 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
             const bool ok = valid(j);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
-                kr[bb][ks] = ok ? *(const u32x4*)(kc + (size_t)j * D + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+                R.k[bb][ks] = ok ? *(const u32x4*)(kc + (size_t)j * D + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int e = 0; e < KPL; ++e) {
             const int j = kb + KPL * kq + e;
-            vr[e] = valid(j) ? *(const u32x4*)(vc + (size_t)j * D + 8 * cc) : u32x4{0, 0, 0, 0};
+            R.v[e] = valid(j) ? *(const u32x4*)(vc + (size_t)j * D + 8 * cc) : u32x4{0, 0, 0, 0};
         }
     };
 
-    if (st0 < st1) load(st0);
-    for (int st = st0; st < st1; ++st) {
+    auto step = [&](StepRegs& R, int st) __attribute__((always_inline)) {
+        auto& kr = R.k;
+        auto& vr = R.v;
         const int kb = j0 + st * KW;
         if (rope) {
 #pragma unroll
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
                 ((u32x2*)sm.vt[wave])[(dim * (KW / 8) + ((kq >> 1) ^ vswz(dim))) * 2 + (kq & 1)] = cell;
             }
         }
-        if (st + 1 < st1) load(st + 1);
+        if (st + DEPTH < st1) load(R, st + DEPTH);
 
         const bool step_full = all_valid && kb + KW <= j1;
         if (!step_full) {
@@ -285,6 +292,20 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
             const int dim = 16 * db + col;
             const u32x4 x = sm.vt[wave][dim * (KW / 8) + (g ^ vswz(dim))];
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), pb, oacc[db], 0, 0, 0);
+        }
+    };
+
+    if constexpr (DEPTH == 1) {
+        StepRegs A;
+        if (st0 < st1) load(A, st0);
+        for (int st = st0; st < st1; ++st) step(A, st);
+    } else {
+        StepRegs A, Bf;
+        if (st0 < st1) load(A, st0);
+        if (st0 + 1 < st1) load(Bf, st0 + 1);
+        for (int st = st0; st < st1; st += 2) {
+            step(A, st);
+            if (st + 1 < st1) step(Bf, st + 1);
         }
     }
 
@@ -349,7 +370,10 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
     const unsigned nblk = (unsigned)a.B * a.Hkv * a.n_split;
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(nblk), dim3(NT), 0, st, a);
+    if (a.rope_log2_base > 0.0)
+        hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(nblk), dim3(NT), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(nblk), dim3(NT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((unsigned)a.B * a.Hq), dim3(D), 0, st, a);
