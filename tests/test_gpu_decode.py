@@ -193,8 +193,10 @@ def test_decode_split_counts_agree(gpu):
 
 def test_workload4_full(gpu):
     """Workload 4 at full size: 8192-token pre-fill in one append call (most of
-    it superseded), cache bit-exact; 1024 decode steps, sampled steps checked
-    against the oracle."""
+    it superseded), cache bit-exact; 1024 decode steps (even steps as
+    cache_append + decode, odd steps as the fused decode_step, the bench's
+    launch), sampled steps of both kinds checked against the oracle, and the
+    final cache bit-exact."""
     import sliding_window_attention_sink_amd as swa
     w = si.WORKLOADS[4]
     hk, hv = si.decode_history(w)
@@ -215,10 +217,13 @@ def test_workload4_full(gpu):
     say("workload 4 steps")
     for i in range(w.steps):
         T = w.L + i + 1
-        swa.cache_append(kd[i].unsqueeze(2), vd[i].unsqueeze(2), kc, vc, T - 1, w.s, w.r)
-        swa.decode(qd[i], kc, vc, T, w.s, w.r, out=outs[i])
+        if i % 2 == 0:
+            swa.cache_append(kd[i].unsqueeze(2), vd[i].unsqueeze(2), kc, vc, T - 1, w.s, w.r)
+            swa.decode(qd[i], kc, vc, T, w.s, w.r, out=outs[i])
+        else:
+            swa.decode_step(qd[i], kd[i], vd[i], kc, vc, T, w.s, w.r, out=outs[i])
     torch.cuda.synchronize()
-    check = {0: 64, 1: 64, 511: 64, 1023: None}
+    check = {0: 64, 1: 64, 510: 64, 511: 64, 1023: None}
     g = np.random.default_rng(4)
     for i in range(w.steps):
         sim.append(ks[i][:, :, None], vs[i][:, :, None], w.L + i)

@@ -183,6 +183,20 @@ def test_dilated_prefill_matches_oracle(gpu, case):
     assert max_err(host(o), ref) <= TOL[dtype]
 
 
+def test_dilated_main_workload_sampled_rows(gpu):
+    """Dilation 4 on the main workload's tensors at full size (L = 8192,
+    32/8 heads): sampled rows, plus the first and last rows of one head."""
+    import sliding_window_attention_sink_amd as swa
+    w = si.WORKLOADS[2]
+    q, k, v = si.prefill_inputs(w)
+    say("dilated main workload")
+    o = host(swa.prefill_dilated(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), w.s, w.r, 4))
+    rows = sample_rows(w.B, w.Hq, w.L, 200, 31)
+    ref = oracle.prefill_rows(q, k, v, w.s, w.r, rows=rows, dilation=4)
+    got = np.stack([o[b, h, t] for b, h, t in rows])
+    assert max_err(got, ref) <= TOL["bf16"]
+
+
 def test_dilation_one_is_plain_prefill(gpu):
     import sliding_window_attention_sink_amd as swa
     q, k, v = case_inputs(65, 1, 4, 2, 400, 128, "bf16")
