@@ -429,6 +429,50 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     const std::integral_constant<bool, true> K_;
     const std::integral_constant<bool, false> V_;
 
+    // The tiles of the last phase are one arithmetic run, key tile vo0 + v.
+    // Two sub-runs are fixed once per work item so the steady state spends
+    // a range check per tile instead of re-deriving the tile's class:
+    //   [vf_lo, vf_hi]: every row of the tile is needed by some query of the
+    //     workgroup and lies in the call's own tokens, so a tile is one
+    //     contiguous 16 KB read (the first branch of issue());
+    //   [vx_lo, vx_hi]: every key of the tile is in U(t) of every row of this
+    //     wave, so its scores take no mask (cluster_x's full tile).
+    // Tiles outside them (sinks, band edges, the cache) take the general code.
+    const Phase PL = nph >= 2 ? ph1 : ph0;
+    const int vo = nph >= 2 ? n0 : 0;
+    const int vo0 = PL.first - vo;
+    auto cdiv = [](int x) __attribute__((always_inline)) { return x >= 0 ? (x + BN - 1) / BN : -((-x) / BN); };
+    auto fdiv = [](int x) __attribute__((always_inline)) { return x >= 0 ? x / BN : -((-x + BN - 1) / BN); };
+    int vf_lo = 0, vf_hi = -1, vx_lo = 0, vx_hi = -1;
+    if (nph > 0 && PL.band_lo != NO_BAND) {
+        const int lo_any = PL.band_lo > t0 - r + 1 ? PL.band_lo : t0 - r + 1;
+        const int ca = cdiv(lo_any), cp = cdiv(pos0);
+        vf_lo = (ca > cp ? ca : cp) - vo0;
+        vf_lo = vf_lo > vo ? vf_lo : vo;
+        vf_hi = fdiv(t1 - (BN - 1)) - vo0;
+        vf_hi = vf_hi < nv - 1 ? vf_hi : nv - 1;
+        const int lo_w1 = PL.band_lo > tw1 - r + 1 ? PL.band_lo : tw1 - r + 1;
+        vx_lo = cdiv(lo_w1) - vo0;
+        vx_lo = vx_lo > vo ? vx_lo : vo;
+        vx_hi = fdiv(tw0 - (BN - 1)) - vo0;
+        vx_hi = vx_hi < nv - 1 ? vx_hi : nv - 1;
+    }
+    // issue() with the contiguous run taken by a pointer step
+    auto issue_run = [&](auto is_k_c, int v, int set) __attribute__((always_inline)) {
+        constexpr bool is_k = decltype(is_k_c)::value;
+        const int vv = v < nv ? v : nv - 1;
+        if (vv >= vf_lo && vv <= vf_hi) {
+            const __bf16* base = (is_k ? kn : vn) + (size_t)(BN * (vo0 + vv) - pos0) * D;
+            u32x4* dst0 = is_k ? smem[set].k : smem[set].v;
+            const uint32_t off = is_k ? kloff : vloff;
+#pragma unroll
+            for (int j = 0; j < T::JN; ++j)
+                load_lds16_off(base, off + (uint32_t)(T::JSTEP * T::RB * j), dst0 + 64 * (sub + GW * j));
+        } else {
+            issue(is_k_c, v, set);
+        }
+    };
+
     // ---- per-wave state
     typename T::QRegs qr;
     int q_loaded = -1;
@@ -464,27 +508,31 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // the wave needs the tile); the mask is applied only to tiles that are
     // not inside every row's key set.
     auto cluster_x = [&](int v) __attribute__((always_inline)) {
-        const Phase P = phase_of(v);
-        const int kb = tile_of(v) * BN;
-        const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
-        const int lo_w1 = P.band_lo > tw1 - r + 1 ? P.band_lo : tw1 - r + 1;
-        const bool need = kb <= tw1 && (kb < P.sink_hi || kb + 63 >= lo_w0);
-        if (!need) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
-            return;
-        }
-        const bool full = kb + 63 <= tw0 && (kb >= lo_w1 || kb + 63 < P.sink_hi);
         const float NEG = -__builtin_inff();
-        if (!full) {
-            const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
-            const int kbg = kb + 8 * g;
-            const int lim_t = my_t - kbg, lim_s = P.sink_hi - kbg, lim_b = lo_me - kbg;
+        // tiles in [vx_lo, vx_hi] are needed and mask-free for every row of
+        // the wave; only the others are classified here
+        if (v < vx_lo || v > vx_hi) {
+            const Phase P = phase_of(v);
+            const int kb = tile_of(v) * BN;
+            const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
+            const int lo_w1 = P.band_lo > tw1 - r + 1 ? P.band_lo : tw1 - r + 1;
+            const bool need = kb <= tw1 && (kb < P.sink_hi || kb + 63 >= lo_w0);
+            if (!need) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
-                sacc0[i] = (k0 <= lim_t && (k0 < lim_s || k0 >= lim_b)) ? sacc0[i] : NEG;
-                sacc1[i] = (k1 <= lim_t && (k1 < lim_s || k1 >= lim_b)) ? sacc1[i] : NEG;
+                for (int i = 0; i < 4; ++i) pk[i] = bf16x8{};
+                return;
+            }
+            const bool full = kb + 63 <= tw0 && (kb >= lo_w1 || kb + 63 < P.sink_hi);
+            if (!full) {
+                const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
+                const int kbg = kb + 8 * g;
+                const int lim_t = my_t - kbg, lim_s = P.sink_hi - kbg, lim_b = lo_me - kbg;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
+                    sacc0[i] = (k0 <= lim_t && (k0 < lim_s || k0 >= lim_b)) ? sacc0[i] : NEG;
+                    sacc1[i] = (k1 <= lim_t && (k1 < lim_s || k1 >= lim_b)) ? sacc1[i] : NEG;
+                }
             }
         }
         // P against the running max first: while this lane's weights of the
@@ -562,24 +610,35 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // then the softmax of tile vx
     auto x_half = [&](auto is_k_c, int vx, int v, int nset) __attribute__((always_inline)) {
         n_last = T::JN;
-        issue(is_k_c, decltype(is_k_c)::value ? v + 2 : v + 1, nset);
+        issue_run(is_k_c, decltype(is_k_c)::value ? v + 2 : v + 1, nset);
         if (wave_active && vx >= 0) cluster_x(vx);
     };
 
+    // Whether some row of this wave has a key of tile v in its key set.  The
+    // products of a tile no row needs are skipped (its scores would be
+    // dropped and its weights are zero): the workgroup visits the union of
+    // its waves' tiles, and matrix work saved is power the clock keeps.
+    auto wave_needs = [&](int v) __attribute__((always_inline)) -> bool {
+        if (v >= vx_lo && v <= vx_hi) return true;
+        const Phase P = phase_of(v);
+        const int kb = tile_of(v) * BN;
+        const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
+        return kb <= tw1 && (kb < P.sink_hi || kb + BN - 1 >= lo_w0);
+    };
     auto c_first = [&]() __attribute__((always_inline)) {
-        if (wave_active) {
+        if (wave_active && wave_needs(0)) {
             ensure_q(0);
             T::template cluster<true, false>(smem[0], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
         }
     };
     auto c_mid = [&](int v, int set) __attribute__((always_inline)) {
-        if (wave_active) {
+        if (wave_active && (wave_needs(v) || wave_needs(v - 1))) {
             ensure_q(v);
             T::template cluster<true, true>(smem[set], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
         }
     };
     auto c_last = [&](int set) __attribute__((always_inline)) {
-        if (wave_active)
+        if (wave_active && wave_needs(nv - 1))
             T::template cluster<false, true>(smem[set], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
     };
     if (nv > 0) {
