@@ -101,17 +101,57 @@ class LaunchTimer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
 
 
+SETTLE_MS = 150.0
+
+
+class Settler:
+    """Brings the GPU clock to its loaded level before a timed region.
+
+    After an idle spell (here: staging each workload's inputs on the CPU) the
+    graphics clock ramps up over the first ~20 ms of load: on the main
+    workload the first 50 back-to-back launches run at ~0.45 ms each, every
+    later one at ~0.38 ms.  Each timed region is therefore preceded by
+    SETTLE_MS of back-to-back launches of the main prefill kernel on random
+    tensors of the main workload's shape (untimed; the steady-state rate is
+    what the metric asks for, and the cold rate is reported beside it)."""
+
+    def __init__(self, torch, swa, w, ms: float = SETTLE_MS):
+        self.torch, self.swa, self.w, self.ms = torch, swa, w, ms
+        self.t = None
+
+    def __call__(self):
+        torch, w, ms = self.torch, self.w, self.ms
+        if self.t is None:
+            g = torch.Generator(device="cuda").manual_seed(7)
+            q = torch.randn((w.B, w.Hq, w.L, w.d), generator=g, device="cuda").to(torch.bfloat16)
+            k = torch.randn((w.B, w.Hkv, w.L, w.d), generator=g, device="cuda").to(torch.bfloat16)
+            v = torch.randn((w.B, w.Hkv, w.L, w.d), generator=g, device="cuda").to(torch.bfloat16)
+            self.t = (q, k, v, torch.empty_like(q))
+        q, k, v, o = self.t
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(8):
+                self.swa.prefill(q, k, v, w.s, w.r, out=o)
+            torch.cuda.synchronize()
+
+
+def _no_settle():
+    return None
+
+
 def to_dev(torch, x, dtype):
     return torch.from_numpy(x).to("cuda").to(dtype).contiguous()
 
 
-def bench_prefill(torch, swa, w, steps, warmup):
+def bench_prefill(torch, swa, w, steps, warmup, settle=_no_settle):
     q, k, v = __import__("swa_inputs").prefill_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qd, kd, vd = to_dev(torch, q, dt), to_dev(torch, k, dt), to_dev(torch, v, dt)
     del q, k, v
     out = torch.empty_like(qd)
     stream = torch.cuda.current_stream()
+    settle()
     for _ in range(warmup):
         swa.prefill(qd, kd, vd, w.s, w.r, out=out)
     torch.cuda.synchronize()
@@ -130,7 +170,7 @@ def bench_prefill(torch, swa, w, steps, warmup):
     return {"ms": ms, "kernel_ms": ms, "flops": flops, "tflops": flops / ms / 1e9}
 
 
-def bench_window_sweep(torch, swa, w, windows, steps=10):
+def bench_window_sweep(torch, swa, w, windows, steps=10, settle=_no_settle):
     """Prefill of the main workload's tensors at several window sizes r (s as
     given), up to r >= L, i.e. full causal attention: time and cache size."""
     q, k, v = __import__("swa_inputs").prefill_inputs(w)
@@ -139,6 +179,7 @@ def bench_window_sweep(torch, swa, w, windows, steps=10):
     out = torch.empty_like(qd)
     stream = torch.cuda.current_stream()
     res = {}
+    settle()
     for r in windows:
         for _ in range(2):
             swa.prefill(qd, kd, vd, w.s, r, out=out)
@@ -165,7 +206,7 @@ def dilated_key_count_sum(L: int, s: int, r: int, dil: int) -> int:
     return int((np.minimum(s, t + 1) + win).sum())
 
 
-def bench_dilated(torch, swa, w, dilations, steps=10):
+def bench_dilated(torch, swa, w, dilations, steps=10, settle=_no_settle):
     """Dilated-window prefill of the main workload's tensors (gather, banded
     prefill of the residue classes, scatter), algorithmic TFLOP/s."""
     q, k, v = __import__("swa_inputs").prefill_inputs(w)
@@ -175,6 +216,7 @@ def bench_dilated(torch, swa, w, dilations, steps=10):
     desc = swa.make_desc(w.B, w.Hq, w.Hkv, w.d, w.s, w.r, torch.bfloat16)
     stream = torch.cuda.current_stream()
     res = {}
+    settle()
     for dil in dilations:
         ws = torch.empty(max(16, swa._lib.swa_prefill_dilated_workspace_bytes(desc, w.L, dil)), dtype=torch.uint8,
                          device="cuda")
@@ -195,7 +237,7 @@ def bench_dilated(torch, swa, w, dilations, steps=10):
     return res
 
 
-def bench_decode(torch, swa, w, steps=None):
+def bench_decode(torch, swa, w, steps=None, settle=_no_settle):
     si = __import__("swa_inputs")
     steps = w.steps if steps is None else steps
     hk, hv = si.decode_history(w)
@@ -222,6 +264,7 @@ def bench_decode(torch, swa, w, steps=None):
         swa.decode(qd[i], kc2, vc2, w.L + i + 1, w.s, w.r, out=out, workspace=ws)
     torch.cuda.synchronize()
     del kc2, vc2
+    settle()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     # the same steps as separate append and decode launches, on a copy of
@@ -271,7 +314,7 @@ def bench_decode(torch, swa, w, steps=None):
             "gbs": step_bytes / ms / 1e6, "decode_kernel_bytes": kv + qo}
 
 
-def bench_chunked(torch, swa, w, reps=2):
+def bench_chunked(torch, swa, w, reps=2, settle=_no_settle):
     si = __import__("swa_inputs")
     q, k, v = si.chunk_inputs(w, 0, w.L)
     qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
@@ -299,6 +342,7 @@ def bench_chunked(torch, swa, w, reps=2):
 
     one_pass()
     torch.cuda.synchronize()
+    settle()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
@@ -349,6 +393,8 @@ def main():
                          "main workload, 7 = its dilated-window prefill, or 'none')")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's 1024)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed back-to-back main-kernel launches before each timed region, in ms (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -379,21 +425,22 @@ def main():
 
     w = si.WORKLOADS[2]
     log("main workload", w.name)
-    main_res = bench_prefill(torch, swa, w, args.steps, args.warmup)
+    settle = Settler(torch, swa, w, args.settle_ms) if args.settle_ms > 0 else _no_settle
+    main_res = bench_prefill(torch, swa, w, args.steps, args.warmup, settle)
     log("main", main_res)
 
     extra = {}
     todo = set() if (args.only_main or args.extra == "none") else {int(x) for x in args.extra.split(",") if x}
     if 3 in todo:
         w3 = si.WORKLOADS[3]
-        r3 = bench_prefill(torch, swa, w3, max(5, args.steps // 2), 2)
+        r3 = bench_prefill(torch, swa, w3, max(5, args.steps // 2), 2, settle)
         extra[w3.name] = {"tflops": r3["tflops"], "ms": r3["ms"], "kernel_ms": r3["kernel_ms"],
                           "frac_bf16_peak": r3["tflops"] / PEAK_BF16_TFLOPS}
         log("w3", r3)
         torch.cuda.empty_cache()
     if 4 in todo:
         w4 = si.WORKLOADS[4]
-        r4 = bench_decode(torch, swa, w4, args.decode_steps)
+        r4 = bench_decode(torch, swa, w4, args.decode_steps, settle)
         dec_gbs = r4["decode_kernel_bytes"] / r4["decode_ms"] / 1e6
         extra[w4.name] = {"GB/s": r4["gbs"], "us_per_step": r4["ms"] * 1e3, "steps": r4["steps"],
                           "us_per_step_separate_append_decode": r4["ms_separate"] * 1e3,
@@ -406,22 +453,30 @@ def main():
         torch.cuda.empty_cache()
     if 5 in todo:
         w5 = si.WORKLOADS[5]
-        r5 = bench_chunked(torch, swa, w5)
+        r5 = bench_chunked(torch, swa, w5, settle=settle)
         extra[w5.name] = {"tflops": r5["tflops"], "ms": r5["ms"], "frac_bf16_peak": r5["tflops"] / PEAK_BF16_TFLOPS,
                           "prefill_call_ms": r5["prefill_call_ms"]}
         log("w5", r5)
         torch.cuda.empty_cache()
     if 6 in todo:
         # window sweep on the main workload's tensors, to the full-attention limit
-        extra["window_sweep_" + w.name] = bench_window_sweep(torch, swa, w, [512, 1024, 2048, 4096, 8192])
+        extra["window_sweep_" + w.name] = bench_window_sweep(torch, swa, w, [512, 1024, 2048, 4096, 8192], settle=settle)
         torch.cuda.empty_cache()
     if 7 in todo:
-        extra["dilated_" + w.name] = bench_dilated(torch, swa, w, [2, 4])
+        extra["dilated_" + w.name] = bench_dilated(torch, swa, w, [2, 4], settle=settle)
         torch.cuda.empty_cache()
     if 1 in todo:
         w1 = si.WORKLOADS[1]
-        r1 = bench_prefill(torch, swa, w1, 20, 3)
+        r1 = bench_prefill(torch, swa, w1, 20, 3, settle)
         extra[w1.name] = {"tflops": r1["tflops"], "ms": r1["ms"], "frac_f32_peak": r1["tflops"] / PEAK_F32_TFLOPS}
+
+    if todo:
+        # the same measurement from a cold start: after an idle second, no
+        # settle phase (the clock is still ramping during these launches)
+        time.sleep(1.0)
+        rc = bench_prefill(torch, swa, w, args.steps, args.warmup)
+        extra["main_cold_start"] = {"ms": rc["ms"], "tflops": rc["tflops"], "frac_bf16_peak": rc["tflops"] / PEAK_BF16_TFLOPS}
+        log("main cold", rc)
 
     achieved = main_res["flops"] / main_res["kernel_ms"] / 1e9
     line = {
@@ -442,6 +497,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": MAIN_KERNEL, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": recorded_traffic()},
+        "settle_ms": args.settle_ms,
         "extra": extra,
     }
     if not args.no_cpu_baseline:
