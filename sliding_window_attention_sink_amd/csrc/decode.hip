@@ -195,6 +195,10 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
         u32x4 v[KPL];
     };
     constexpr int DEPTH = ROPE ? 1 : 2;
+    // K and V are streamed with the non-temporal hint: every cache byte is
+    // read once per step, so keeping it out of the caches leaves them to the
+    // reads that do repeat (measured on the 64-sequence workload: 6.7 TB/s
+    // against 5.8 with default caching)
     auto load = [&](StepRegs& R, int st) __attribute__((always_inline)) {
         const int kb = j0 + st * KW;
 #pragma unroll
@@ -203,12 +207,14 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
             const bool ok = valid(j);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
-                R.k[bb][ks] = ok ? *(const u32x4*)(kc + (size_t)j * D + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+                R.k[bb][ks] = ok ? __builtin_nontemporal_load((const u32x4*)(kc + (size_t)j * D + 32 * ks + 8 * g))
+                                 : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int e = 0; e < KPL; ++e) {
             const int j = kb + KPL * kq + e;
-            R.v[e] = valid(j) ? *(const u32x4*)(vc + (size_t)j * D + 8 * cc) : u32x4{0, 0, 0, 0};
+            R.v[e] = valid(j) ? __builtin_nontemporal_load((const u32x4*)(vc + (size_t)j * D + 8 * cc))
+                              : u32x4{0, 0, 0, 0};
         }
     };
 
