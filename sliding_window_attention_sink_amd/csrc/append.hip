@@ -27,8 +27,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a, int64_t n_sin
         const int64_t slot = p < a.s ? p : a.s + p % a.r;
         const int64_t src = ((bh * a.n) + (p - a.pos0)) * chunks + c;
         const int64_t dst = ((bh * (a.s + a.r)) + slot) * chunks + c;
-        ((u32x4*)a.kc)[dst] = ((const u32x4*)a.kn)[src];
-        ((u32x4*)a.vc)[dst] = ((const u32x4*)a.vn)[src];
+        // the new tokens are read once: non-temporal, so they do not displace
+        // cache lines that are read again
+        ((u32x4*)a.kc)[dst] = __builtin_nontemporal_load((const u32x4*)a.kn + src);
+        ((u32x4*)a.vc)[dst] = __builtin_nontemporal_load((const u32x4*)a.vn + src);
     }
 }
 

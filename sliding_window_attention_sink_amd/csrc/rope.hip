@@ -76,7 +76,10 @@ __global__ __launch_bounds__(256) void rope_prepare_kernel(RopeArgs a) {
     const int rows_per_pass = 256 / TPR;
     const int rsub = tid / TPR, j0 = (tid % TPR) * 8;
     auto rot = [&](const __bf16* src, __bf16* dst, int which) {
-        const u32x4 lo = *(const u32x4*)(src + j0), hi = *(const u32x4*)(src + j0 + H2);
+        // each source row is read once (non-temporal); the rotated copies are
+        // read by the attention kernel right after, so they are stored normally
+        const u32x4 lo = __builtin_nontemporal_load((const u32x4*)(src + j0)),
+                    hi = __builtin_nontemporal_load((const u32x4*)(src + j0 + H2));
         u32x4 olo, ohi;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
