@@ -81,12 +81,12 @@ def test_chunk_size_independence_and_resume(gpu):
     assert max_err(host(a), host(b)) <= TOL["bf16"]
 
 
-def test_workload5_full(gpu):
-    """Workload 5 at full size (131072 tokens in 32 chunks of 4096, RoPE base
-    1e4): every 64th row, all heads, against the oracle."""
+def test_chunked_rope_131072_full(gpu):
+    """Chunked streaming prefill at full size (B=1, H=32, d=128, 131072 tokens
+    in 32 chunks of 4096, s=4, r=4092, RoPE base 1e4): every 64th row, all heads, against the oracle."""
     w = si.WORKLOADS[5]
     q, k, v = si.chunk_inputs(w, 0, w.L)
-    say("workload 5 full")
+    say("chunked prefill full size", w.name)
     o = run_chunked(q, k, v, w.s, w.r, w.chunk, w.rope_base)
     t = np.arange(0, w.L, w.check_every)
     rows = np.array([[0, h, tt] for h in range(w.Hq) for tt in t])

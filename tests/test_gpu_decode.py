@@ -191,8 +191,8 @@ def test_decode_split_counts_agree(gpu):
         assert max_err(o, ref) <= TOL["bf16"], ns
 
 
-def test_workload4_full(gpu):
-    """Workload 4 at full size: 8192-token pre-fill in one append call (most of
+def test_decode_b64_gqa_full(gpu):
+    """Decode at full size (B=64, GQA 32/8, d=128, s=4, r=4092): 8192-token pre-fill in one append call (most of
     it superseded), cache bit-exact; 1024 decode steps (even steps as
     cache_append + decode, odd steps as the fused decode_step, the bench's
     launch), sampled steps of both kinds checked against the oracle, and the
@@ -200,7 +200,7 @@ def test_workload4_full(gpu):
     import sliding_window_attention_sink_amd as swa
     w = si.WORKLOADS[4]
     hk, hv = si.decode_history(w)
-    say("workload 4 pre-fill")
+    say("decode full size: pre-fill", w.name)
     kc, vc = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda", fill=float("nan"))
     hkd, hvd = dev(hk, "bf16"), dev(hv, "bf16")
     swa.cache_append(hkd, hvd, kc, vc, 0, w.s, w.r)
@@ -214,7 +214,7 @@ def test_workload4_full(gpu):
     qs, ks, vs = si.decode_steps(w)
     qd, kd, vd = dev(qs, "bf16"), dev(ks, "bf16"), dev(vs, "bf16")
     outs = torch.empty((w.steps, w.B, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
-    say("workload 4 steps")
+    say("decode full size: steps", w.name)
     for i in range(w.steps):
         T = w.L + i + 1
         if i % 2 == 0:

@@ -63,10 +63,10 @@ def test_prefill_matches_oracle(gpu, case):
             assert max_err(o, want) <= 1e-6
 
 
-def test_workload1_all_rows(gpu):
+def test_prefill_f32_l256_all_rows(gpu):
     w = si.WORKLOADS[1]
     q, k, v = si.prefill_inputs(w)
-    say("workload 1", w.name)
+    say("fp32 prefill", w.name)
     o = host(run_prefill(q, k, v, w.s, w.r, w.dtype))
     ref = oracle.prefill_rows(q, k, v, w.s, w.r).reshape(o.shape)
     assert max_err(o, ref) <= TOL["f32"]
@@ -83,12 +83,13 @@ def sample_rows(B, H, L, n, seed, edge=130):
 
 @pytest.mark.parametrize("wid", [2, 3])
 def test_full_workload_sampled_rows(gpu, wid):
-    """Full-size workloads 2 and 3, in the launch configuration the benchmark
-    times, checked on sampled rows (every head touched at random rows, plus
+    """Full-size bf16 prefills (GQA 32/8, L=8192, s=0, r=4096; and B=4, H=32,
+    L=16384, s=4, r=1020), in the launch configuration the benchmark times,
+    checked on sampled rows (every head touched at random rows, plus
     the first and last query tiles of two heads)."""
     w = si.WORKLOADS[wid]
     q, k, v = si.prefill_inputs(w)
-    say("workload", wid, w.name)
+    say("prefill", w.name)
     o_dev = run_prefill(q, k, v, w.s, w.r, w.dtype)
     rows = sample_rows(w.B, w.Hq, w.L, 3000, wid)
     got = host(o_dev[rows[:, 0], rows[:, 1], rows[:, 2]])
