@@ -316,19 +316,24 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
 
     // ---- work item
     const int w = xcd_work_item(blockIdx.x, gridDim.x);
-    const int mt = a.n_mtiles - 1 - (w % a.n_mtiles);   // late (heavier) query tiles first
-    const int rest = w / a.n_mtiles;
-    int b, kvh, h, row0, tok;
+    // Late (heavier) query tiles first.  In pair mode the q-head pairs of a
+    // kv-head are the innermost index: the pairs of one query tile read the
+    // same K/V tiles, so running them side by side halves the key range in
+    // flight on an XCD and its L2 keeps the tiles for their second reader.
+    int mt, b, kvh, h, row0, tok;
     if (a.pair_mode) {
         const int npairs = G / 2;
-        const int pair = rest % npairs, bk = rest / npairs;
+        const int pair = w % npairs, rest = w / npairs;
+        mt = a.n_mtiles - 1 - (rest % a.n_mtiles);
+        const int bk = rest / a.n_mtiles;
         b = bk / a.Hkv;
         kvh = bk % a.Hkv;
         h = kvh * G + 2 * pair + grp;
         tok = 128;
         row0 = mt * tok;
     } else {
-        const int bh = rest;
+        mt = a.n_mtiles - 1 - (w % a.n_mtiles);
+        const int bh = w / a.n_mtiles;
         b = bh / a.Hq;
         h = bh % a.Hq;
         kvh = h / G;
