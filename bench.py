@@ -66,6 +66,24 @@ def recorded_traffic():
     return int(m_b.group(1))
 
 
+MFMA_NOTE = os.path.join(ROOT, "profiles", "prefill_pp_kernel_gqa32x8_L8192_mfma.md")
+
+
+def recorded_mfma_busy():
+    """Fraction of the main kernel's cycles with the matrix units busy, from
+    the SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE counter note, or None if
+    absent or stale."""
+    try:
+        text = open(MFMA_NOTE).read()
+    except OSError:
+        return None
+    m_u = re.search(r"^mfma_busy_frac:\s*([0-9.]+)\s*$", text, re.M)
+    m_h = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    if not (m_u and m_h) or m_h.group(1) != kernel_sources_sha256():
+        return None
+    return float(m_u.group(1))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -496,7 +514,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": MAIN_KERNEL, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic()},
+                     "traffic": recorded_traffic(), "mfma_busy_frac": recorded_mfma_busy()},
         "settle_ms": args.settle_ms,
         "extra": extra,
     }
