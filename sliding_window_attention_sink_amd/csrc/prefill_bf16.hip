@@ -357,7 +357,23 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
 
     // ---- tiles of the workgroup: phase 0 then phase 1, as one list
     Phase ph0 = {0, -1, 0, NO_BAND, 0}, ph1 = {0, -1, 0, NO_BAND, 0};
-    const int nph = make_phases(t0, t1, s, r, a.merge_sink != 0, ph0, ph1);
+    int nph = make_phases(t0, t1, s, r, a.merge_sink != 0, ph0, ph1);
+    // Sink packing.  When the sinks would take a tile of their own (they do
+    // not touch the band) and the band's first tile starts with at least s
+    // keys that every row of the workgroup masks (the keys below
+    // t0 - r + 1), the s sink rows are loaded into those slots and the sink
+    // tile is dropped: one phase whose keys kb0 .. kb0+s-1 stand for sinks
+    // 0 .. s-1.  Only with one set of queries for both (no RoPE).
+    int pack_lo = NO_BAND;
+    if (a.merge_sink && nph == 2) {
+        const int kb0 = ph1.first * BN;
+        const int lo = s > t0 - r + 1 ? s : t0 - r + 1;
+        if (lo - kb0 >= s) {
+            pack_lo = kb0;
+            ph0 = Phase{ph1.first, ph1.last, kb0 + s, s, 0};
+            nph = 1;
+        }
+    }
     const int n0 = nph >= 1 ? ph0.last - ph0.first + 1 : 0;
     const int n1 = nph >= 2 ? ph1.last - ph1.first + 1 : 0;
     const int nv = n0 + n1;
@@ -419,6 +435,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
             for (int j = 0; j < T::JN; ++j) {
                 int p = kbase + key0 + T::JSTEP * j;
                 p = (p >= P.sink_hi && p < lo_any) ? gap_to : p;
+                p = (p >= pack_lo && p < P.sink_hi) ? p - pack_lo : p;   // packed sink slot -> sink row
                 p = p < t1 ? p : t1;
                 const __bf16* rowp;
                 if (p >= pos0) {

@@ -41,6 +41,13 @@ CASES = [
     (11, "bf16", 1, 2, 2, 128, 7, 4, 2),
     (12, "bf16", 1, 8, 1, 128, 389, 1, 64),
     (13, "bf16", 1, 2, 2, 128, 1, 4, 28),
+    # sinks packed into the masked head of the first band tile: with r = 100
+    # every later query block masks 29 keys there (256-row and 128-row
+    # blocks alike), so s = 4 and s = 29 pack and s = 30 keeps its own tile
+    (14, "bf16", 1, 2, 2, 128, 1500, 4, 100),
+    (15, "bf16", 1, 4, 2, 128, 1100, 29, 100),
+    (16, "bf16", 1, 4, 2, 128, 1100, 30, 100),
+    (17, "bf16", 2, 2, 2, 64, 1300, 4, 100),
 ]
 
 
