@@ -10,7 +10,9 @@
 //   * sink j < s is min(t, s+r-1) - j before the query: rotate it to j and,
 //     for sink scores only, the query to min(t, s+r-1).
 // This kernel writes those rotated copies once per call (bf16, rotated in
-// fp32 from fp64 angles so that positions up to 2^31 keep full accuracy):
+// fp32; the angle position * theta is formed in fp64 and reduced to its
+// fraction of a turn before the fp32 sine and cosine, so positions up to
+// 2^31 keep full accuracy):
 //   qb  = q rotated to t,  qs = q rotated to min(t, s+r-1),
 //   knr = chunk keys rotated to their position,
 //   kcr = cache keys rotated to the position of the token each slot holds.
@@ -61,12 +63,13 @@ __global__ __launch_bounds__(256) void rope_prepare_kernel(RopeArgs a) {
     const int tid = threadIdx.x;
     if (tid < 2 * H2) {
         const int which = tid / H2, j = tid % H2;
-        const double theta = exp2(-(2.0 * j / D) * log2((double)a.base));
-        const double ang = (double)(which ? pos_b : pos_a) * theta;
-        double sd, cd;
-        sincos(ang, &sd, &cd);
-        cs[which][j] = (float)cd;
-        sn[which][j] = (float)sd;
+        // turns per position of pair j, then the fraction of a turn at the
+        // position (the hardware sine and cosine take turns)
+        const double turns = exp2(-(2.0 * j / D) * log2((double)a.base)) * 0.15915494309189535;
+        const double rv = (double)(which ? pos_b : pos_a) * turns;
+        const float x = (float)(rv - __builtin_floor(rv));
+        cs[which][j] = __builtin_amdgcn_cosf(x);
+        sn[which][j] = __builtin_amdgcn_sinf(x);
     }
     __syncthreads();
 
@@ -75,11 +78,7 @@ __global__ __launch_bounds__(256) void rope_prepare_kernel(RopeArgs a) {
     constexpr int TPR = H2 / 8;
     const int rows_per_pass = 256 / TPR;
     const int rsub = tid / TPR, j0 = (tid % TPR) * 8;
-    auto rot = [&](const __bf16* src, __bf16* dst, int which) {
-        // each source row is read once (non-temporal); the rotated copies are
-        // read by the attention kernel right after, so they are stored normally
-        const u32x4 lo = __builtin_nontemporal_load((const u32x4*)(src + j0)),
-                    hi = __builtin_nontemporal_load((const u32x4*)(src + j0 + H2));
+    auto rot_to = [&](const u32x4& lo, const u32x4& hi, __bf16* dst, int which) {
         u32x4 olo, ohi;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -101,12 +100,25 @@ __global__ __launch_bounds__(256) void rope_prepare_kernel(RopeArgs a) {
         *(u32x4*)(dst + j0) = olo;
         *(u32x4*)(dst + j0 + H2) = ohi;
     };
+    // each source row is read once (non-temporal); the rotated copies are
+    // read by the attention kernel right after, so they are stored normally
+    auto load_row = [&](const __bf16* src, u32x4& lo, u32x4& hi) {
+        lo = __builtin_nontemporal_load((const u32x4*)(src + j0));
+        hi = __builtin_nontemporal_load((const u32x4*)(src + j0 + H2));
+    };
+    auto rot = [&](const __bf16* src, __bf16* dst, int which) {
+        u32x4 lo, hi;
+        load_row(src, lo, hi);
+        rot_to(lo, hi, dst, which);
+    };
     if (is_row) {
-        // queries: B*Hq rows at chunk row `item`
+        // queries: B*Hq rows at chunk row `item`, read once, rotated twice
         for (int rr = rsub; rr < a.B * a.Hq; rr += rows_per_pass) {
             const size_t off = ((size_t)rr * L + item) * D;
-            rot((const __bf16*)a.q + off, (__bf16*)a.qb + off, 0);
-            rot((const __bf16*)a.q + off, (__bf16*)a.qsk + off, 1);
+            u32x4 lo, hi;
+            load_row((const __bf16*)a.q + off, lo, hi);
+            rot_to(lo, hi, (__bf16*)a.qb + off, 0);
+            rot_to(lo, hi, (__bf16*)a.qsk + off, 1);
         }
         for (int rr = rsub; rr < a.B * a.Hkv; rr += rows_per_pass) {
             const size_t off = ((size_t)rr * L + item) * D;
