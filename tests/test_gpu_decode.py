@@ -237,3 +237,37 @@ def test_decode_b64_gqa_full(gpu):
             err = max_err(np.stack([got[b, h] for b, h in pairs]), ref)
             assert err <= TOL["bf16"], (i, err)
     assert_cache_equal(kc, vc, sim)
+
+
+def test_decode_rope_full_size_sampled(gpu):
+    """The RoPE-re-positioning generation step at the bench's size (B=64,
+    GQA 32/8, d=128, s=4, r=4092, 8192-token history): 8 fused steps on the
+    pre-rotation cache, every head of two sequences checked against the fp64
+    row definition (keys of U(t) at cache positions 0..|U(t)|-1)."""
+    import sliding_window_attention_sink_amd as swa
+    w = si.WORKLOADS[4]
+    base, nsteps, pick = 1e4, 8, [3, w.B - 1]
+    hk, hv = si.decode_history(w)
+    qs, ks, vs = si.decode_steps(w, steps=nsteps)
+    say("decode rope full size: pre-fill", w.name)
+    kc, vc = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda", fill=float("nan"))
+    hkd, hvd = dev(hk, "bf16"), dev(hv, "bf16")
+    swa.cache_append(hkd, hvd, kc, vc, 0, w.s, w.r)
+    torch.cuda.synchronize()
+    del hkd, hvd
+    qd, kd, vd = dev(qs, "bf16"), dev(ks, "bf16"), dev(vs, "bf16")
+    outs = torch.empty((nsteps, w.B, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
+    say("decode rope full size: steps", w.name)
+    for i in range(nsteps):
+        swa.decode_step(qd[i], kd[i], vd[i], kc, vc, w.L + i + 1, w.s, w.r, rope_base=base, out=outs[i])
+    torch.cuda.synchronize()
+    got = host(outs)[:, pick]                                   # [steps, 2, Hq, d]
+    # the two sequences' full token streams, for the oracle's row definition
+    T = w.L + nsteps
+    K = np.concatenate([hk[pick], ks[:, pick].transpose(1, 2, 0, 3)], axis=2)
+    V = np.concatenate([hv[pick], vs[:, pick].transpose(1, 2, 0, 3)], axis=2)
+    Q = np.zeros((len(pick), w.Hq, T, w.d), dtype=np.float32)
+    Q[:, :, w.L:] = qs[:, pick].transpose(1, 2, 0, 3)
+    rows = np.array([[b, h, w.L + i] for i in range(nsteps) for b in range(len(pick)) for h in range(w.Hq)])
+    ref = oracle.prefill_rows(Q, K, V, w.s, w.r, rope_base=base, rows=rows).reshape(nsteps, len(pick), w.Hq, w.d)
+    assert max_err(got, ref) <= TOL["bf16"]
