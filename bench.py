@@ -84,6 +84,23 @@ def recorded_mfma_busy():
     return float(m_u.group(1))
 
 
+SCLK_NOTE = os.path.join(ROOT, "profiles", "prefill_pp_kernel_gqa32x8_L8192_sclk.md")
+
+
+def recorded_sclk():
+    """Shader clock (GHz) during the main kernel's timed launches, from the
+    GRBM_COUNT note, or None if absent or stale."""
+    try:
+        text = open(SCLK_NOTE).read()
+    except OSError:
+        return None
+    m_c = re.search(r"^sclk_ghz_timed:\s*([0-9.]+)\s*$", text, re.M)
+    m_h = re.search(r"^kernel_sources_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    if not (m_c and m_h) or m_h.group(1) != kernel_sources_sha256():
+        return None
+    return float(m_c.group(1))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -497,6 +514,7 @@ def main():
         log("main cold", rc)
 
     achieved = main_res["flops"] / main_res["kernel_ms"] / 1e9
+    sclk = recorded_sclk()
     line = {
         "metric": "SWA+sink prefill TFLOP/s and decode KV GB/s, % of roofline, 1 MI355X",
         "value": main_res["tflops"],
@@ -514,7 +532,9 @@ def main():
                    "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": MAIN_KERNEL, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": recorded_traffic(), "mfma_busy_frac": recorded_mfma_busy()},
+                     "traffic": recorded_traffic(), "mfma_busy_frac": recorded_mfma_busy(),
+                     "sclk_ghz_observed": sclk,
+                     "frac_at_observed_sclk": (achieved / (PEAK_BF16_TFLOPS * sclk / 2.4)) if sclk else None},
         "settle_ms": args.settle_ms,
         "extra": extra,
     }
