@@ -395,6 +395,45 @@ def bench_chunked(torch, swa, w, reps=2, settle=_no_settle):
     return {"ms": ms, "flops": flops, "tflops": flops / ms / 1e9, "prefill_call_ms": timer.mean_ms()}
 
 
+def bench_decode_window_sweep(torch, swa, w, slots=(1024, 2048, 4096, 8192, 32768), settle=_no_settle):
+    """Decode launch time against the cache size, on the decode workload's
+    shape (B sequences, GQA, d, s sinks): caches of s + r slots for several
+    r, the largest being full attention over a 32768-token context.  Time
+    and KV bytes scale with the slots; the cache of a 4096-token window is
+    8x smaller than the full cache at 32K context.  Random bf16 caches (the
+    decode reads every valid slot; the values do not change the work)."""
+    out_res = {}
+    g = torch.Generator(device="cuda").manual_seed(11)
+    q = torch.randn((w.B, w.Hq, w.d), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for S in slots:
+        r = S - w.s
+        kc = torch.randn((w.B, w.Hkv, S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        vc = torch.randn((w.B, w.Hkv, S, w.d), generator=g, device="cuda").to(torch.bfloat16)
+        desc = swa.make_desc(w.B, w.Hq, w.Hkv, w.d, w.s, r, torch.bfloat16)
+        ws = torch.empty(max(16, swa.decode_workspace_bytes(desc)), dtype=torch.uint8, device="cuda")
+        T = S + 100                                      # every slot valid
+        for _ in range(3):
+            swa.decode(q, kc, vc, T, w.s, r, out=out, workspace=ws)
+        settle()
+        n = 32
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(n):
+            swa.decode(q, kc, vc, T, w.s, r, out=out, workspace=ws)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / n
+        kv = w.B * w.Hkv * S * w.d * 2 * 2
+        out_res["slots%d" % S] = {"us": ms * 1e3, "kv_bytes": kv, "GB/s": (kv + 2 * w.B * w.Hq * w.d * 2) / ms / 1e6,
+                                  "full_attention_32k": S == 32768}
+        del kc, vc, ws
+        torch.cuda.empty_cache()
+    return out_res
+
+
 def cpu_baseline(w, budget_s: float):
     """The fp64 oracle, as it stands, on random rows of the main workload."""
     import oracle
@@ -423,9 +462,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time the main workload only")
-    ap.add_argument("--extra", default="3,4,5,6,7,1",
+    ap.add_argument("--extra", default="3,4,5,6,7,8,1",
                     help="other workloads to time alongside (comma list of 1,3,4,5, 6 = window sweep of the "
-                         "main workload, 7 = its dilated-window prefill, or 'none')")
+                         "main workload, 7 = its dilated-window prefill, 8 = decode against the cache size, "
+                         "or 'none')")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's 1024)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
@@ -499,6 +539,10 @@ def main():
         torch.cuda.empty_cache()
     if 7 in todo:
         extra["dilated_" + w.name] = bench_dilated(torch, swa, w, [2, 4], settle=settle)
+        torch.cuda.empty_cache()
+    if 8 in todo:
+        w4 = si.WORKLOADS[4]
+        extra["decode_window_sweep_" + w4.name] = bench_decode_window_sweep(torch, swa, w4, settle=settle)
         torch.cuda.empty_cache()
     if 1 in todo:
         w1 = si.WORKLOADS[1]
