@@ -479,12 +479,34 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         vx_hi = fdiv(tw0 - (BN - 1)) - vo0;
         vx_hi = vx_hi < nv - 1 ? vx_hi : nv - 1;
     }
-    // issue() with the contiguous run taken by a pointer step
+    // The same for the rolling part of the cache (chunked calls): tiles in
+    // [vc_lo, vc_hi] have every row needed and all keys in [s, pos0), so
+    // tile v holds slots s + (rel(v) .. rel(v) + 63) with rel(v) = key mod r.
+    // A band covers fewer than r cached keys, so the run wraps at most once;
+    // a tile that does not straddle the wrap is 64 contiguous slots.
+    int vc_lo = 0, vc_hi = -1, relc0 = 0;
+    if (kc != nullptr && nph > 0 && PL.band_lo != NO_BAND) {
+        const int lo_any = PL.band_lo > t0 - r + 1 ? PL.band_lo : t0 - r + 1;
+        const int ca = cdiv(lo_any), cs = cdiv(s);
+        vc_lo = (ca > cs ? ca : cs) - vo0;
+        vc_lo = vc_lo > vo ? vc_lo : vo;
+        vc_hi = fdiv(pos0 - BN) - vo0;
+        vc_hi = vc_hi < nv - 1 ? vc_hi : nv - 1;
+        if (vc_lo <= vc_hi) relc0 = (BN * (vo0 + vc_lo)) % r;
+    }
+    // issue() with the contiguous runs taken by a pointer step
     auto issue_run = [&](auto is_k_c, int v, int set) __attribute__((always_inline)) {
         constexpr bool is_k = decltype(is_k_c)::value;
         const int vv = v < nv ? v : nv - 1;
+        const __bf16* base = nullptr;
         if (vv >= vf_lo && vv <= vf_hi) {
-            const __bf16* base = (is_k ? kn : vn) + (size_t)(BN * (vo0 + vv) - pos0) * D;
+            base = (is_k ? kn : vn) + (size_t)(BN * (vo0 + vv) - pos0) * D;
+        } else if (vv >= vc_lo && vv <= vc_hi) {
+            int rel = relc0 + BN * (vv - vc_lo);
+            rel = rel >= r ? rel - r : rel;
+            if (rel + BN <= r) base = (is_k ? kc : vc) + (size_t)(s + rel) * D;
+        }
+        if (base != nullptr) {
             u32x4* dst0 = is_k ? smem[set].k : smem[set].v;
             const uint32_t off = is_k ? kloff : vloff;
 #pragma unroll
