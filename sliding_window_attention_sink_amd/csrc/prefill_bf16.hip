@@ -571,11 +571,32 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
                 const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
                 const int kbg = kb + 8 * g;
                 const int lim_t = my_t - kbg, lim_s = P.sink_hi - kbg, lim_b = lo_me - kbg;
+                // Most cut tiles hold no sinks and cut one edge only: the
+                // diagonal (every row's window reaches below the tile: keep
+                // k <= t) or the window's lower edge (the tile is below every
+                // row: keep k >= t - r + 1); one compare per score there.
+                const bool no_sink = kb >= P.sink_hi;
+                if (no_sink && kb >= lo_w1) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
-                    sacc0[i] = (k0 <= lim_t && (k0 < lim_s || k0 >= lim_b)) ? sacc0[i] : NEG;
-                    sacc1[i] = (k1 <= lim_t && (k1 < lim_s || k1 >= lim_b)) ? sacc1[i] : NEG;
+                    for (int i = 0; i < 16; ++i) {
+                        const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
+                        sacc0[i] = k0 <= lim_t ? sacc0[i] : NEG;
+                        sacc1[i] = k1 <= lim_t ? sacc1[i] : NEG;
+                    }
+                } else if (no_sink && kb + 63 <= tw0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
+                        sacc0[i] = k0 >= lim_b ? sacc0[i] : NEG;
+                        sacc1[i] = k1 >= lim_b ? sacc1[i] : NEG;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
+                        sacc0[i] = (k0 <= lim_t && (k0 < lim_s || k0 >= lim_b)) ? sacc0[i] : NEG;
+                        sacc1[i] = (k1 <= lim_t && (k1 < lim_s || k1 >= lim_b)) ? sacc1[i] : NEG;
+                    }
                 }
             }
         }
