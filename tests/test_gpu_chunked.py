@@ -57,6 +57,21 @@ def test_chunked_matches_oracle(gpu, rope_base, chunk):
     assert err <= TOL["bf16"], f"max-abs error {err}"
 
 
+@pytest.mark.parametrize("rope_base", [0.0, 10000.0])
+@pytest.mark.parametrize("Hq,Hkv,chunk", [(4, 2, 500), (2, 2, 1000)])
+def test_chunked_long_window_cache_tiles(gpu, rope_base, Hq, Hkv, chunk):
+    """Bands with many cached key tiles: r = 700 slots (the wrap falls inside
+    a 64-key tile), chunk starts not on tile boundaries, GQA pairs and MHA;
+    the contiguous cache-tile loads and the straddling tile's per-row path."""
+    B, L, d, s, r = 1, 3000, 128, 4, 700
+    q, k, v = seq_inputs(12, B, Hq, Hkv, L, d)
+    say("chunked long window", Hq, Hkv, chunk, rope_base)
+    o = host(run_chunked(q, k, v, s, r, chunk, rope_base))
+    ref = oracle.chunked_rows(q, k, v, s, r, rope_base=rope_base, rows=None).reshape(o.shape)
+    err = max_err(o, ref)
+    assert err <= TOL["bf16"], f"max-abs error {err}"
+
+
 def test_single_chunk_rope_equals_plain_rope_prefill(gpu):
     """One chunk holding the whole sequence: the RoPE path without a cache."""
     import sliding_window_attention_sink_amd as swa
