@@ -452,7 +452,20 @@ def cpu_baseline(w, budget_s: float):
         batch = min(batch * 2, 16384)
     flops = 4.0 * w.d * done_keys
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "%d random query rows of %s (%d keys), fp64, %.1f s" % (done_rows, w.name, done_keys, elapsed)}
+            "sample": "%d random query rows of %s (%d keys), fp64, %.1f s" % (done_rows, w.name, done_keys, elapsed),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
