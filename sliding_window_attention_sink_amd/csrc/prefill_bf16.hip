@@ -452,14 +452,17 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     const std::integral_constant<bool, false> V_;
 
     // The tiles of the last phase are one arithmetic run, key tile vo0 + v.
-    // Two sub-runs are fixed once per work item so the steady state spends
-    // a range check per tile instead of re-deriving the tile's class:
+    // Sub-runs are fixed once per work item so the steady state spends a
+    // range check per tile instead of re-deriving the tile's class:
     //   [vf_lo, vf_hi]: every row of the tile is needed by some query of the
     //     workgroup and lies in the call's own tokens, so a tile is one
     //     contiguous 16 KB read (the first branch of issue());
     //   [vx_lo, vx_hi]: every key of the tile is in U(t) of every row of this
-    //     wave, so its scores take no mask (cluster_x's full tile).
-    // Tiles outside them (sinks, band edges, the cache) take the general code.
+    //     wave, so its scores take no mask (cluster_x's full tile);
+    //   [vc_lo, vc_hi] (below): the same as the first for the rolling part
+    //     of the cache.
+    // Tiles outside them (sinks, band edges, a tile straddling the cache's
+    // wrap) take the general code.
     const Phase PL = nph >= 2 ? ph1 : ph0;
     const int vo = nph >= 2 ? n0 : 0;
     const int vo0 = PL.first - vo;
@@ -682,7 +685,8 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // Whether some row of this wave has a key of tile v in its key set.  The
     // products of a tile no row needs are skipped (its scores would be
     // dropped and its weights are zero): the workgroup visits the union of
-    // its waves' tiles, and matrix work saved is power the clock keeps.
+    // its waves' tiles, and the matrix work saved also lets the clock run
+    // higher.
     auto wave_needs = [&](int v) __attribute__((always_inline)) -> bool {
         if (v >= vx_lo && v <= vx_hi) return true;
         const Phase P = phase_of(v);
