@@ -7,6 +7,7 @@ imports it, and it imports nothing from the product package.
 from .oracle import (  # noqa: F401
     RollingCacheSim,
     attend_set,
+    backward,
     build,
     chunked_rows,
     decode_row,

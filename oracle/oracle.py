@@ -177,3 +177,55 @@ def decode_row(cache: RollingCacheSim, q, b: int, h: int, Hq: int, *, scale: flo
     kvh = h // (Hq // Hkv)
     sl = cache.valid_slots()
     return attend_set(q, cache.k[b, kvh, sl], cache.v[b, kvh, sl], scale=scale)
+
+
+def backward(q, k, v, o, do, s: int, r: int, *, scale: float | None = None):
+    """Gradients of the prefill rows with respect to q, k and v, fp64.
+
+    The forward is row t = softmax over U(t) of scale * q_t . k_i, weighting
+    v_i (hyper.ai summary, section on sliding-window attention with sinks;
+    t6page eq:attn-fixed-streaming for the key set).  For an upstream
+    gradient dO its derivative, written out per (batch, q-head) with the key
+    set as a 0/1 mask M[t, i] = [i in U(t)]:
+
+        P  = softmax_rows(scale * Q K^T restricted to M)
+        dV = P^T dO                      (summed over the q-heads of a kv-head)
+        dP = dO V^T
+        D_t = sum_j dO[t, j] * O[t, j]   (O as the caller passes it)
+        dS = P * (dP - D)
+        dQ = scale * dS K,   dK = scale * dS^T Q   (dK summed over the group)
+
+    ``o`` is the forward output the caller holds (the same O enters D on
+    both sides); q, k, v, o, do: [B, Hq|Hkv, L, d].  Returns (dq, dk, dv) in
+    fp64 with the shapes of q, k, v.
+    """
+    q, k, v, o, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, o, do))
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, L, d) or v.shape != k.shape or o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    mask = np.zeros((L, L), dtype=bool)
+    for t in range(L):
+        mask[t, key_set(t, s, r)] = True
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // G
+            S = scale * (q[b, h] @ k[b, kvh].T)
+            S = np.where(mask, S, -np.inf)
+            P = np.exp(S - S.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dv[b, kvh] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, kvh].T
+            D = (do[b, h] * o[b, h]).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[b, h] = scale * (dS @ k[b, kvh])
+            dk[b, kvh] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv
