@@ -165,6 +165,32 @@ int swa_decode_step(const swa_desc* desc, const void* q, const void* k_new, cons
                     void* v_cache, int64_t T, void* o, int32_t n_split, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * Backward of swa_prefill without a cache or RoPE (training): the gradients
+ * of the rows O with respect to q, k and v for an upstream gradient dout.
+ * The rows are softmax over U(t) of scale * q_t . k_i weighting v_i (the
+ * hyper.ai summary's section on sliding-window attention with sinks,
+ * eq:attn-fixed-streaming on the t6page page); the gradient is that
+ * definition's derivative:
+ *   dV_i = sum_t P_ti dout_t,  dS_ti = P_ti (dout_t . v_i - dout_t . o_t),
+ *   dQ_t = scale sum_i dS_ti k_i,  dK_i = scale sum_t dS_ti q_t,
+ * over the pairs with i in U(t), dK and dV summed over the q-heads of each
+ * kv-head.  o is the forward output the caller holds (it enters
+ * dout_t . o_t; pass swa_prefill's output).  P is recomputed from q and k.
+ * Inputs bf16 (desc->dtype = SWA_BF16): q, o, dout [B, Hq, L, d]; k, v
+ * [B, Hkv, L, d].  Outputs fp32, caller-owned, fully overwritten: dq
+ * [B, Hq, L, d]; dk, dv [B, Hkv, L, d].  Workspace: at least
+ * swa_backward_workspace_bytes() bytes (per-row log-sum-exp and
+ * dout . o), 16-byte aligned.  Sink keys' gradients are accumulated with
+ * fp32 atomics, so their rounding order may differ from call to call.
+ * Errors: SWA_ERR_INVALID_ARG (null or misaligned pointer, L < 1, short
+ * workspace, shape fields), SWA_ERR_UNSUPPORTED (d, fp32 inputs, RoPE),
+ * SWA_ERR_HIP.
+ */
+size_t swa_backward_workspace_bytes(const swa_desc* desc, int64_t L);
+int swa_backward(const swa_desc* desc, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 float* dq, float* dk, float* dv, int64_t L, void* workspace, size_t workspace_bytes, void* stream);
+
 /* The split count swa_decode uses for n_split = 0. */
 int32_t swa_decode_default_splits(const swa_desc* desc);
 

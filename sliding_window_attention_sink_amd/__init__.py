@@ -10,11 +10,13 @@ of include/swa.h); this package binds it for PyTorch callers:
   * decode(q, kc, vc, T, s, r, ...)    split-K single-query decode
   * decode_step(q, k, v, kc, vc, T, s, r, ...) append token T-1 and decode
                                        it in one launch
+  * backward(q, k, v, o, dout, s, r)   gradients of prefill's rows (training)
 
 The low-level same-name wrappers of the C functions are in ``_lib``.
 """
 from ._lib import EXPORTS, LIB_PATH, SwaDesc, SwaError, load  # noqa: F401
 from .ops import (  # noqa: F401
+    backward,
     cache_append,
     decode,
     decode_step,

@@ -23,7 +23,8 @@ SWA_BF16 = 1
 EXPORTS = (
     "swa_prefill_workspace_bytes", "swa_prefill", "swa_cache_append", "swa_decode_workspace_bytes",
     "swa_decode", "swa_decode_step", "swa_decode_default_splits", "swa_prefill_dilated_workspace_bytes",
-    "swa_prefill_dilated", "swa_status_str", "swa_last_error", "swa_abi_version",
+    "swa_prefill_dilated", "swa_backward_workspace_bytes", "swa_backward", "swa_status_str", "swa_last_error",
+    "swa_abi_version",
 )
 
 
@@ -71,6 +72,10 @@ def load() -> ctypes.CDLL:
     lib.swa_prefill_dilated_workspace_bytes.restype = sz
     lib.swa_prefill_dilated.argtypes = [dp, i32, vp, vp, vp, vp, i64, vp, sz, vp]
     lib.swa_prefill_dilated.restype = ctypes.c_int
+    lib.swa_backward_workspace_bytes.argtypes = [dp, i64]
+    lib.swa_backward_workspace_bytes.restype = sz
+    lib.swa_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
+    lib.swa_backward.restype = ctypes.c_int
     lib.swa_decode_default_splits.argtypes = [dp]
     lib.swa_decode_default_splits.restype = i32
     lib.swa_status_str.argtypes = [ctypes.c_int]
@@ -128,6 +133,15 @@ def swa_prefill_dilated_workspace_bytes(desc: SwaDesc, L: int, dilation: int) ->
 
 def swa_prefill_dilated(desc, dilation, q, k, v, o, L, workspace, workspace_bytes, stream) -> int:
     return load().swa_prefill_dilated(ctypes.byref(desc), dilation, q, k, v, o, L, workspace, workspace_bytes, stream)
+
+
+def swa_backward_workspace_bytes(desc: SwaDesc, L: int) -> int:
+    return load().swa_backward_workspace_bytes(ctypes.byref(desc), L)
+
+
+def swa_backward(desc, q, k, v, o, dout, dq, dk, dv, L, workspace, workspace_bytes, stream) -> int:
+    return load().swa_backward(ctypes.byref(desc), q, k, v, o, dout, dq, dk, dv, L, workspace, workspace_bytes,
+                               stream)
 
 
 def swa_status_str(status: int) -> str:

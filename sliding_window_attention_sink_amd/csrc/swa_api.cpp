@@ -407,3 +407,62 @@ int swa_decode_step(const swa_desc* desc, const void* q, const void* k_new, cons
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t swa_backward_workspace_bytes(const swa_desc* desc, int64_t L) {
+    if (check_desc(desc, "swa_backward_workspace_bytes") != SWA_OK || L < 1 || L > kMaxPos) return 0;
+    return round_up((size_t)2 * desc->B * desc->Hq * (size_t)L * sizeof(float), 256);
+}
+
+int swa_backward(const swa_desc* desc, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 float* dq, float* dk, float* dv, int64_t L, void* workspace, size_t workspace_bytes, void* stream) {
+    static const char* fn = "swa_backward";
+    clear_error();
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    if (desc->dtype != SWA_BF16) return fail(SWA_ERR_UNSUPPORTED, "%s: the backward is built for bf16 inputs", fn);
+    if (desc->rope_base > 0.0f) return fail(SWA_ERR_UNSUPPORTED, "%s: the backward with RoPE is not built", fn);
+    if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k, fn, "k")) || (st = check_ptr(v, fn, "v")) ||
+        (st = check_ptr(o, fn, "o")) || (st = check_ptr(dout, fn, "dout")) || (st = check_ptr(dq, fn, "dq")) ||
+        (st = check_ptr(dk, fn, "dk")) || (st = check_ptr(dv, fn, "dv")) ||
+        (st = check_ptr(workspace, fn, "workspace")))
+        return st;
+    if (L < 1) return fail(SWA_ERR_INVALID_ARG, "%s: L must be >= 1 (got %lld)", fn, (long long)L);
+    if (L > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
+    const size_t rows = (size_t)desc->B * desc->Hq * (size_t)L;
+    const size_t need = round_up(2 * rows * sizeof(float), 256);
+    if (workspace_bytes < need)
+        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    // one wave per row (and per key, per sink segment), four per workgroup
+    if ((rows + 3) / 4 > 0x7fffffffULL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
+    if ((int64_t)(desc->Hq / desc->Hkv) * L > 0x7fffffffLL)
+        return fail(SWA_ERR_INVALID_ARG, "%s: L * (Hq / Hkv) beyond 2^31", fn);
+    if (desc->s > 0 && L > desc->r) {
+        const size_t sink_items = (size_t)desc->B * desc->Hkv * desc->s * ((L - desc->r + swa::kSinkSeg - 1) / swa::kSinkSeg);
+        if ((sink_items + 3) / 4 > 0x7fffffffULL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
+    }
+
+    swa::BackwardArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.lse2 = static_cast<float*>(workspace);
+    a.dd = a.lse2 + rows;
+    a.L = L;
+    a.B = desc->B;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.s = desc->s;
+    a.r = desc->r;
+    a.scale = desc->scale;
+    a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
+    return hip_status(swa::launch_backward_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

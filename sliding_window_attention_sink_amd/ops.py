@@ -103,6 +103,36 @@ def prefill_dilated(q, k, v, s, r, dilation, *, scale=None, out=None, workspace=
     return out
 
 
+def backward(q, k, v, o, dout, s, r, *, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv; fp32) of prefill's rows for the upstream dout.
+
+    q, o, dout [B,Hq,L,d] and k, v [B,Hkv,L,d] are bf16; o is prefill's output.
+    """
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale)
+    _need(k, "k", (B, Hkv, L, d), q.dtype, dev)
+    _need(v, "v", (B, Hkv, L, d), q.dtype, dev)
+    _need(o, "o", q.shape, q.dtype, dev)
+    _need(dout, "dout", q.shape, q.dtype, dev)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    _need(dq, "dq", q.shape, torch.float32, dev)
+    _need(dk, "dk", k.shape, torch.float32, dev)
+    _need(dv, "dv", k.shape, torch.float32, dev)
+    wsb = _lib.swa_backward_workspace_bytes(desc, L)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    check(_lib.swa_backward(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), L,
+                            _ptr(workspace), workspace.numel(), _stream(dev, stream)))
+    return dq, dk, dv
+
+
 def cache_append(k_new, v_new, k_cache, v_cache, pos0, s, r, *, stream=None):
     """Write tokens pos0 .. pos0+n-1 (k_new/v_new [B,Hkv,n,d]) into the rolling cache."""
     B, Hkv, n, d = k_new.shape

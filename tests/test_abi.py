@@ -155,6 +155,25 @@ def test_prefill_dilated_rejects():
     assert dil(L=0) == -1
 
 
+def test_backward_rejects():
+    d_ = desc()
+    wsb = _lib.swa_backward_workspace_bytes(d_, 100)
+    assert wsb == 2 * 1 * 4 * 100 * 4 + 256 - (2 * 1 * 4 * 100 * 4) % 256   # two floats a row, 256-byte rounded
+    G1, G2, G3 = 0x80000, 0x90000, 0xA0000
+
+    def bwd(dd=d_, q=A, dq=G1, ws=W, n=wsb, L=100):
+        return _lib.swa_backward(dd, q, B_, C, D, E, dq, G2, G3, L, ws, n, None)
+
+    assert bwd(q=None) == -1 and "q is NULL" in _lib.swa_last_error()
+    assert bwd(dq=G1 + 8) == -1 and "aligned" in _lib.swa_last_error()
+    assert bwd(ws=None) == -1 and "workspace" in _lib.swa_last_error()
+    assert bwd(n=wsb - 16) == -1 and "workspace" in _lib.swa_last_error()
+    assert bwd(L=0) == -1 and "L must be" in _lib.swa_last_error()
+    assert bwd(dd=desc(dtype=_lib.SWA_F32)) == -2 and "bf16" in _lib.swa_last_error()
+    assert bwd(dd=desc(rope_base=1e4)) == -2 and "RoPE" in _lib.swa_last_error()
+    assert bwd(dd=desc(d=96)) == -2
+
+
 def test_last_error_is_per_call():
     assert prefill(desc(r=0)) == -1
     assert _lib.swa_last_error() != ""
