@@ -10,8 +10,8 @@ sink + window key set count, 4*d flops each.  Alongside it (under "extra")
 the same run times the StreamingLLM 4+1020 prefill (B=4, H=32, L=16384), the
 rolling-buffer decode loop (B=64, 32/8 heads, 4+4092 slots, append + decode
 per step, as one fused launch and as two) and the chunked RoPE streaming prefill (131072 tokens in chunks of
-4096).  The "cpu_baseline" leg times the fp64 oracle on a bounded sample of
-the main workload's rows.
+4096) and the main workload's backward (dq, dk, dv).  The "cpu_baseline"
+leg times the fp64 oracle on a bounded sample of the main workload's rows.
 
 Prints exactly one JSON line on stdout.
 """
@@ -272,6 +272,40 @@ def bench_dilated(torch, swa, w, dilations, steps=10, settle=_no_settle):
     return res
 
 
+def bench_backward(torch, swa, w, steps=3, settle=_no_settle):
+    """Backward (dq, dk, dv) of the main workload's rows for a random upstream
+    gradient.  Algorithmic flops: 10 d per (query, key) pair of the key set
+    (scores, dout.v, and the dq, dk, dv products); the kernels execute 16 d
+    (the scores three times, dout.v twice) in fp32 vector arithmetic."""
+    q, k, v = __import__("swa_inputs").prefill_inputs(w)
+    qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
+    del q, k, v
+    g = torch.Generator(device="cuda").manual_seed(11)
+    dod = torch.randn(qd.shape, device="cuda", generator=g).to(torch.bfloat16)
+    od = swa.prefill(qd, kd, vd, w.s, w.r)
+    dq = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(kd.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(kd.shape, dtype=torch.float32, device="cuda")
+    desc = swa.make_desc(w.B, w.Hq, w.Hkv, w.d, w.s, w.r, torch.bfloat16)
+    ws = torch.empty(swa._lib.swa_backward_workspace_bytes(desc, w.L), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    swa.backward(qd, kd, vd, od, dod, w.s, w.r, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    settle()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        swa.backward(qd, kd, vd, od, dod, w.s, w.r, dq=dq, dk=dk, dv=dv, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    pairs = key_count_sum(w.L, w.s, w.r) * w.B * w.Hq
+    return {"ms": ms, "tflops": 10.0 * w.d * pairs / ms / 1e9,
+            "executed_fp32_tflops": 16.0 * w.d * pairs / ms / 1e9,
+            "frac_fp32_vector_peak": 16.0 * w.d * pairs / ms / 1e9 / PEAK_F32_TFLOPS}
+
+
 def bench_decode(torch, swa, w, steps=None, settle=_no_settle):
     si = __import__("swa_inputs")
     steps = w.steps if steps is None else steps
@@ -475,10 +509,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time the main workload only")
-    ap.add_argument("--extra", default="3,4,5,6,7,8,1",
+    ap.add_argument("--extra", default="3,4,5,6,7,8,9,1",
                     help="other workloads to time alongside (comma list of 1,3,4,5, 6 = window sweep of the "
                          "main workload, 7 = its dilated-window prefill, 8 = decode against the cache size, "
-                         "or 'none')")
+                         "9 = the main workload's backward, or 'none')")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's 1024)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
@@ -556,6 +590,10 @@ def main():
     if 8 in todo:
         w4 = si.WORKLOADS[4]
         extra["decode_window_sweep_" + w4.name] = bench_decode_window_sweep(torch, swa, w4, settle=settle)
+        torch.cuda.empty_cache()
+    if 9 in todo:
+        extra["backward_" + w.name] = bench_backward(torch, swa, w, settle=settle)
+        log("backward", extra["backward_" + w.name])
         torch.cuda.empty_cache()
     if 1 in todo:
         w1 = si.WORKLOADS[1]

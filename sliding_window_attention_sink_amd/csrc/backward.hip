@@ -25,7 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "swa_internal.h"
+#include "backward_internal.h"
 
 namespace swa {
 namespace {
@@ -39,25 +39,32 @@ constexpr int BT = 64 * BW;
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// x (fp32, LDS, D values) . row (bf16, global)
+// x (fp32, LDS, D values) . row (bf16, global); four independent chains
+// (element e goes to chain e mod 4), so the result does not depend on which
+// of the two rows sits in LDS
 template <int D>
 __device__ __forceinline__ float dot_row(const float* x, const __bf16* row) {
-    float acc = 0.0f;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll
     for (int c = 0; c < D / 8; ++c) {
         const u32x4 w = *(const u32x4*)(row + 8 * c);
         const f32x4 a = *(const f32x4*)(x + 8 * c);
         const f32x4 b = *(const f32x4*)(x + 8 * c + 4);
-        acc = fmaf(a[0], bf_lo(w[0]), acc);
-        acc = fmaf(a[1], bf_hi(w[0]), acc);
-        acc = fmaf(a[2], bf_lo(w[1]), acc);
-        acc = fmaf(a[3], bf_hi(w[1]), acc);
-        acc = fmaf(b[0], bf_lo(w[2]), acc);
-        acc = fmaf(b[1], bf_hi(w[2]), acc);
-        acc = fmaf(b[2], bf_lo(w[3]), acc);
-        acc = fmaf(b[3], bf_hi(w[3]), acc);
+        a0 = fmaf(a[0], bf_lo(w[0]), a0);
+        a1 = fmaf(a[1], bf_hi(w[0]), a1);
+        a2 = fmaf(a[2], bf_lo(w[1]), a2);
+        a3 = fmaf(a[3], bf_hi(w[1]), a3);
+        a0 = fmaf(b[0], bf_lo(w[2]), a0);
+        a1 = fmaf(b[1], bf_hi(w[2]), a1);
+        a2 = fmaf(b[2], bf_lo(w[3]), a2);
+        a3 = fmaf(b[3], bf_hi(w[3]), a3);
     }
-    return acc;
+    return (a0 + a1) + (a2 + a3);
+}
+
+// lane j's value to every lane (j uniform: a scalar read, no LDS round trip)
+__device__ __forceinline__ float lane_value(float x, int j) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
 }
 
 // This lane's D / 64 consecutive dims of a bf16 row, as fp32.
@@ -145,9 +152,9 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
     const float lse2 = m + log2f(l);
 
     // pass 2: dS of each key (lanes over keys), then dQ (lanes over dims)
-    float acc[NE];
+    float acc[NE], acc2[NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = 0.0f;
+    for (int e = 0; e < NE; ++e) acc[e] = acc2[e] = 0.0f;
     for (int j0 = 0; j0 < n; j0 += 64) {
         const int j = j0 + lane;
         float ds = 0.0f;
@@ -157,18 +164,24 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
             ds = p * (dot_row<D>(gs, vb + ko) - Dt);
         }
         const int cnt = n - j0 < 64 ? n - j0 : 64;
-#pragma unroll 8
-        for (int jj = 0; jj < cnt; ++jj) {
-            const float g = __shfl(ds, jj);
-            float kx[NE];
-            lane_dims<D>(kb + (int64_t)key_of(j0 + jj) * D, lane, kx);
+        // keys in pairs, one accumulator chain each
+#pragma unroll 4
+        for (int jj = 0; jj < cnt; jj += 2) {
+            const bool two = jj + 1 < cnt;
+            const float g0 = lane_value(ds, jj), g1 = two ? lane_value(ds, jj + 1) : 0.0f;
+            float k0[NE], k1[NE];
+            lane_dims<D>(kb + (int64_t)key_of(j0 + jj) * D, lane, k0);
+            lane_dims<D>(kb + (int64_t)key_of(two ? j0 + jj + 1 : j0 + jj) * D, lane, k1);
 #pragma unroll
-            for (int e = 0; e < NE; ++e) acc[e] = fmaf(g, kx[e], acc[e]);
+            for (int e = 0; e < NE; ++e) {
+                acc[e] = fmaf(g0, k0[e], acc[e]);
+                acc2[e] = fmaf(g1, k1[e], acc2[e]);
+            }
         }
     }
     float* dq = a.dq + row * D + NE * lane;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) dq[e] = acc[e] * a.scale;
+    for (int e = 0; e < NE; ++e) dq[e] = (acc[e] + acc2[e]) * a.scale;
     if (lane == 0) {
         a.lse2[row] = lse2;
         a.dd[row] = Dt;
@@ -197,7 +210,7 @@ __device__ __forceinline__ void kv_sums(const BackwardArgs& a, const float* ks, 
         const int cnt = n - j0 < 64 ? n - j0 : 64;
 #pragma unroll 8
         for (int jj = 0; jj < cnt; ++jj) {
-            const float pj = __shfl(p, jj), gj = __shfl(ds, jj);
+            const float pj = lane_value(p, jj), gj = lane_value(ds, jj);
             const int64_t qr = qrow_of(j0 + jj);
             float gx[NE], qx[NE];
             lane_dims<D>((const __bf16*)a.dout + qr * D, lane, gx);

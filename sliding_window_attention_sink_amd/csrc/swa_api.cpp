@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "swa_internal.h"
+#include "backward_internal.h"
 
 namespace {
 
