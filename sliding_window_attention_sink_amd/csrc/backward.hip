@@ -10,15 +10,16 @@
 //   dQ_t = scale sum_{i in U(t)} dS_ti k_i,   dK_i = scale sum_t dS_ti q_t
 // with dK and dV summed over the q-heads of a kv-head.
 //
-// Three kernels, one wave per row or key, fp32 vector arithmetic (this first
-// backward is correct and plain, not MFMA-tiled):
-//   bwd_q:   per query row, the row's log2-sum-exp over U(t) (one pass over
-//            its keys, lanes over keys), D_t, then dQ_t (a second pass:
-//            lanes score their keys, then lanes over dims add dS_ti k_i);
-//            lse and D go to the workspace.
-//   bwd_kv:  per key i, the queries t = i .. min(L-1, i+r-1) of every q-head
-//            of its group (for i >= s these are all of its queries): dK_i,
-//            dV_i, stored.
+// Three kernels in fp32 vector arithmetic (a plain first backward, not
+// MFMA-tiled); a wave takes eight adjacent rows or keys, so each row a lane
+// reads from memory serves eight dot products:
+//   bwd_q:   per eight query rows, each row's log2-sum-exp over U(t) (one
+//            pass over the union of their keys, lanes over keys), D_t, then
+//            dQ_t (a second pass: lanes score their keys, then lanes over
+//            dims add dS_ti k_i); lse and D go to the workspace.
+//   bwd_kv:  per eight keys, the queries t = i .. min(L-1, i+r-1) of each
+//            key i from every q-head of its group (for i >= s these are all
+//            of its queries): dK_i, dV_i, stored.
 //   bwd_sink: per sink key i < s and segment of the queries t >= i + r (the
 //            sinks are attended by every later query), the same sums, added
 //            atomically after bwd_kv's stores.
@@ -38,29 +39,6 @@ constexpr int BT = 64 * BW;
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// x (fp32, LDS, D values) . row (bf16, global); four independent chains
-// (element e goes to chain e mod 4), so the result does not depend on which
-// of the two rows sits in LDS
-template <int D>
-__device__ __forceinline__ float dot_row(const float* x, const __bf16* row) {
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-        const u32x4 w = *(const u32x4*)(row + 8 * c);
-        const f32x4 a = *(const f32x4*)(x + 8 * c);
-        const f32x4 b = *(const f32x4*)(x + 8 * c + 4);
-        a0 = fmaf(a[0], bf_lo(w[0]), a0);
-        a1 = fmaf(a[1], bf_hi(w[0]), a1);
-        a2 = fmaf(a[2], bf_lo(w[1]), a2);
-        a3 = fmaf(a[3], bf_hi(w[1]), a3);
-        a0 = fmaf(b[0], bf_lo(w[2]), a0);
-        a1 = fmaf(b[1], bf_hi(w[2]), a1);
-        a2 = fmaf(b[2], bf_lo(w[3]), a2);
-        a3 = fmaf(b[3], bf_hi(w[3]), a3);
-    }
-    return (a0 + a1) + (a2 + a3);
-}
 
 // lane j's value to every lane (j uniform: a scalar read, no LDS round trip)
 __device__ __forceinline__ float lane_value(float x, int j) {
@@ -98,102 +76,181 @@ __device__ __forceinline__ void stage2(float* xa, float* xb, const __bf16* ra, c
     }
 }
 
+// R dot products at once: x holds R fp32 rows of D values (LDS, row stride
+// D), row is one bf16 row (global memory), read once for all R.  Elements
+// 0-3 of every 8 go to one accumulator chain and 4-7 to another, so the
+// result does not depend on which operand sits in LDS.
+template <int D, int R>
+__device__ __forceinline__ void dot_rows(const float* x, const __bf16* row, float (&out)[R]) {
+    float c0[R], c1[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) c0[q] = c1[q] = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < D / 8; ++c) {
+        const u32x4 w = *(const u32x4*)(row + 8 * c);
+        const float k0 = bf_lo(w[0]), k1 = bf_hi(w[0]), k2 = bf_lo(w[1]), k3 = bf_hi(w[1]);
+        const float k4 = bf_lo(w[2]), k5 = bf_hi(w[2]), k6 = bf_lo(w[3]), k7 = bf_hi(w[3]);
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const f32x4 a = *(const f32x4*)(x + q * D + 8 * c);
+            const f32x4 b = *(const f32x4*)(x + q * D + 8 * c + 4);
+            c0[q] = fmaf(a[0], k0, c0[q]);
+            c0[q] = fmaf(a[1], k1, c0[q]);
+            c0[q] = fmaf(a[2], k2, c0[q]);
+            c0[q] = fmaf(a[3], k3, c0[q]);
+            c1[q] = fmaf(b[0], k4, c1[q]);
+            c1[q] = fmaf(b[1], k5, c1[q]);
+            c1[q] = fmaf(b[2], k6, c1[q]);
+            c1[q] = fmaf(b[3], k7, c1[q]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) out[q] = c0[q] + c1[q];
+}
+
+// Rows (or keys) per wave in bwd_q and bwd_kv: every K, V, Q or dout row a
+// lane reads serves RW of them (8 ran 11% faster than 4 on the main
+// workload's shape, at 141-179 VGPRs).
+constexpr int RW = 8;
+
 template <int D>
 __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
     constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) float xs[BW][2][D];
+    __shared__ __attribute__((aligned(16))) float xs[BW][2][RW * D];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t nrows = (int64_t)a.B * a.Hq * a.L;
-    const int64_t row = (int64_t)blockIdx.x * BW + wv;     // (b * Hq + h) * L + t
-    if (row >= nrows) return;
-    const int t = (int)(row % a.L);
-    const int64_t bh = row / a.L;
+    const int64_t ngr = (a.L + RW - 1) / RW;                 // row groups per (b, h)
+    const int64_t grp = (int64_t)blockIdx.x * BW + wv;       // (b * Hq + h) * ngr + row group
+    if (grp >= (int64_t)a.B * a.Hq * ngr) return;
+    const int64_t bh = grp / ngr;
+    const int tb = (int)(grp % ngr) * RW;                    // rows tb .. tl
+    const int nr = a.L - tb < RW ? (int)(a.L - tb) : RW;
+    const int tl = tb + nr - 1;
     const int b = (int)(bh / a.Hq), h = (int)(bh % a.Hq);
     const int kvh = h / (a.Hq / a.Hkv);
     const __bf16* kb = (const __bf16*)a.k + ((int64_t)b * a.Hkv + kvh) * a.L * D;
     const __bf16* vb = (const __bf16*)a.v + ((int64_t)b * a.Hkv + kvh) * a.L * D;
-    const __bf16* orow = (const __bf16*)a.o + row * D;
+    const int64_t row0 = bh * a.L + tb;
     float* qs = xs[wv][0];
     float* gs = xs[wv][1];
-    stage2<D>(qs, gs, (const __bf16*)a.q + row * D, (const __bf16*)a.dout + row * D, lane);
+    // rows past the end stage row tl again (their results are not stored)
+#pragma unroll
+    for (int x = 0; x < RW; ++x) {
+        const int64_t rx = row0 + (x < nr ? x : nr - 1);
+        stage2<D>(qs + x * D, gs + x * D, (const __bf16*)a.q + rx * D, (const __bf16*)a.dout + rx * D, lane);
+    }
     lds_order();
-    float dpart = 0.0f;
-    for (int e = lane; e < D; e += 64) dpart += gs[e] * (float)orow[e];
-    const float Dt = wave_sum(dpart);
+    float Dt[RW];
+#pragma unroll
+    for (int x = 0; x < RW; ++x) {
+        const __bf16* orow = (const __bf16*)a.o + (row0 + (x < nr ? x : nr - 1)) * D;
+        float dpart = 0.0f;
+        for (int e = lane; e < D; e += 64) dpart += gs[x * D + e] * (float)orow[e];
+        Dt[x] = wave_sum(dpart);
+    }
 
-    // U(t): sinks 0 .. ns-1, then the window wlo .. t
-    const int ns = a.s < t + 1 ? a.s : t + 1;
-    const int wlo = a.s > t - a.r + 1 ? a.s : t - a.r + 1;
-    const int n = ns + (t >= wlo ? t - wlo + 1 : 0);
+    // keys of any of the rows: sinks 0 .. ns-1, then the window wlo .. tl;
+    // key i is in U(tb + x) iff i <= tb + x and (i < s or i >= tb + x - r + 1)
+    const int ns = a.s < tl + 1 ? a.s : tl + 1;
+    const int wlo = a.s > tb - a.r + 1 ? a.s : tb - a.r + 1;
+    const int n = ns + (tl >= wlo ? tl - wlo + 1 : 0);
     auto key_of = [&](int j) { return j < ns ? j : wlo + (j - ns); };
+    auto in_set = [&](int x, int i) { return x < nr && i <= tb + x && (i < a.s || i >= tb + x - a.r + 1); };
     const float c = a.scale_log2e;
 
-    // pass 1: log2-sum-exp of the row's scores (per lane, then across lanes)
-    float m = -__builtin_inff(), l = 0.0f;
+    // pass 1: log2-sum-exp of each row's scores (per lane, then across lanes)
+    float m[RW], l[RW];
+#pragma unroll
+    for (int x = 0; x < RW; ++x) {
+        m[x] = -__builtin_inff();
+        l[x] = 0.0f;
+    }
     for (int j0 = 0; j0 < n; j0 += 64) {
         const int j = j0 + lane;
         if (j < n) {
-            const float sc = dot_row<D>(qs, kb + (int64_t)key_of(j) * D) * c;
-            if (sc > m) {
-                l = l * exp2f(m - sc) + 1.0f;
-                m = sc;
-            } else {
-                l += exp2f(sc - m);
+            const int i = key_of(j);
+            float sc[RW];
+            dot_rows<D, RW>(qs, kb + (int64_t)i * D, sc);
+#pragma unroll
+            for (int x = 0; x < RW; ++x) {
+                if (!in_set(x, i)) continue;
+                const float v = sc[x] * c;
+                if (v > m[x]) {
+                    l[x] = l[x] * exp2f(m[x] - v) + 1.0f;
+                    m[x] = v;
+                } else {
+                    l[x] += exp2f(v - m[x]);
+                }
             }
         }
     }
+    float lse2[RW];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-        const float mm = fmaxf(m, m2);
-        l = (m == -__builtin_inff() ? 0.0f : l * exp2f(m - mm)) + (m2 == -__builtin_inff() ? 0.0f : l2 * exp2f(m2 - mm));
-        m = mm;
+    for (int x = 0; x < RW; ++x) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float m2 = __shfl_xor(m[x], off), l2 = __shfl_xor(l[x], off);
+            const float mm = fmaxf(m[x], m2);
+            l[x] = (m[x] == -__builtin_inff() ? 0.0f : l[x] * exp2f(m[x] - mm)) +
+                   (m2 == -__builtin_inff() ? 0.0f : l2 * exp2f(m2 - mm));
+            m[x] = mm;
+        }
+        lse2[x] = m[x] + log2f(l[x]);
     }
-    const float lse2 = m + log2f(l);
 
-    // pass 2: dS of each key (lanes over keys), then dQ (lanes over dims)
-    float acc[NE], acc2[NE];
+    // pass 2: dS of each (row, key) (lanes over keys), then dQ (lanes over dims)
+    float acc[RW][NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = acc2[e] = 0.0f;
+    for (int x = 0; x < RW; ++x)
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[x][e] = 0.0f;
     for (int j0 = 0; j0 < n; j0 += 64) {
         const int j = j0 + lane;
-        float ds = 0.0f;
+        float ds[RW];
+#pragma unroll
+        for (int x = 0; x < RW; ++x) ds[x] = 0.0f;
         if (j < n) {
-            const int64_t ko = (int64_t)key_of(j) * D;
-            const float p = exp2f(dot_row<D>(qs, kb + ko) * c - lse2);
-            ds = p * (dot_row<D>(gs, vb + ko) - Dt);
+            const int i = key_of(j);
+            float sc[RW], dp[RW];
+            dot_rows<D, RW>(qs, kb + (int64_t)i * D, sc);
+            dot_rows<D, RW>(gs, vb + (int64_t)i * D, dp);
+#pragma unroll
+            for (int x = 0; x < RW; ++x)
+                if (in_set(x, i)) ds[x] = exp2f(sc[x] * c - lse2[x]) * (dp[x] - Dt[x]);
         }
         const int cnt = n - j0 < 64 ? n - j0 : 64;
-        // keys in pairs, one accumulator chain each
-#pragma unroll 4
-        for (int jj = 0; jj < cnt; jj += 2) {
-            const bool two = jj + 1 < cnt;
-            const float g0 = lane_value(ds, jj), g1 = two ? lane_value(ds, jj + 1) : 0.0f;
-            float k0[NE], k1[NE];
-            lane_dims<D>(kb + (int64_t)key_of(j0 + jj) * D, lane, k0);
-            lane_dims<D>(kb + (int64_t)key_of(two ? j0 + jj + 1 : j0 + jj) * D, lane, k1);
+#pragma unroll 2
+        for (int jj = 0; jj < cnt; ++jj) {
+            float kx[NE];
+            lane_dims<D>(kb + (int64_t)key_of(j0 + jj) * D, lane, kx);
 #pragma unroll
-            for (int e = 0; e < NE; ++e) {
-                acc[e] = fmaf(g0, k0[e], acc[e]);
-                acc2[e] = fmaf(g1, k1[e], acc2[e]);
+            for (int x = 0; x < RW; ++x) {
+                const float g = lane_value(ds[x], jj);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) acc[x][e] = fmaf(g, kx[e], acc[x][e]);
             }
         }
     }
-    float* dq = a.dq + row * D + NE * lane;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) dq[e] = (acc[e] + acc2[e]) * a.scale;
-    if (lane == 0) {
-        a.lse2[row] = lse2;
-        a.dd[row] = Dt;
+    for (int x = 0; x < RW; ++x) {
+        if (x >= nr) break;
+        float* dq = a.dq + (row0 + x) * D + NE * lane;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) dq[e] = acc[x][e] * a.scale;
+        if (lane == 0) {
+            a.lse2[row0 + x] = lse2[x];
+            a.dd[row0 + x] = Dt[x];
+        }
     }
 }
 
-// dK, dV contributions of key i (kv-head kvh of batch b, K and V rows
-// staged in ks, vs) from the queries t0 .. t0+nt-1 of every q-head of the
-// group, added into dka, dva (this lane's dims).
-template <int D>
+// dK, dV contributions of R keys of kv-head kvh of batch b (K and V rows
+// staged in ks, vs, row stride D) from the queries t0 .. t0+nt-1 of every
+// q-head of the group, for the (key x, query t) pairs with ok(x, t); added
+// into dka, dva (this lane's dims).
+template <int D, int R, class Ok>
 __device__ __forceinline__ void kv_sums(const BackwardArgs& a, const float* ks, const float* vs, int b, int kvh,
-                                        int t0, int nt, int lane, float (&dka)[D / 64], float (&dva)[D / 64]) {
+                                        int t0, int nt, int lane, Ok&& ok, float (&dka)[R][D / 64],
+                                        float (&dva)[R][D / 64]) {
     constexpr int NE = D / 64;
     const int G = a.Hq / a.Hkv;
     const int n = nt * G;
@@ -201,24 +258,38 @@ __device__ __forceinline__ void kv_sums(const BackwardArgs& a, const float* ks, 
     auto qrow_of = [&](int j) { return ((int64_t)b * a.Hq + kvh * G + j % G) * a.L + t0 + j / G; };
     for (int j0 = 0; j0 < n; j0 += 64) {
         const int j = j0 + lane;
-        float p = 0.0f, ds = 0.0f;
+        float p[R], ds[R];
+#pragma unroll
+        for (int x = 0; x < R; ++x) p[x] = ds[x] = 0.0f;
         if (j < n) {
             const int64_t qr = qrow_of(j);
-            p = exp2f(dot_row<D>(ks, (const __bf16*)a.q + qr * D) * c - a.lse2[qr]);
-            ds = p * (dot_row<D>(vs, (const __bf16*)a.dout + qr * D) - a.dd[qr]);
+            const int t = t0 + j / G;
+            float sc[R], dp[R];
+            dot_rows<D, R>(ks, (const __bf16*)a.q + qr * D, sc);
+            dot_rows<D, R>(vs, (const __bf16*)a.dout + qr * D, dp);
+            const float l2 = a.lse2[qr], dd = a.dd[qr];
+#pragma unroll
+            for (int x = 0; x < R; ++x) {
+                if (!ok(x, t)) continue;
+                p[x] = exp2f(sc[x] * c - l2);
+                ds[x] = p[x] * (dp[x] - dd);
+            }
         }
         const int cnt = n - j0 < 64 ? n - j0 : 64;
-#pragma unroll 8
+#pragma unroll 2
         for (int jj = 0; jj < cnt; ++jj) {
-            const float pj = lane_value(p, jj), gj = lane_value(ds, jj);
             const int64_t qr = qrow_of(j0 + jj);
             float gx[NE], qx[NE];
             lane_dims<D>((const __bf16*)a.dout + qr * D, lane, gx);
             lane_dims<D>((const __bf16*)a.q + qr * D, lane, qx);
 #pragma unroll
-            for (int e = 0; e < NE; ++e) {
-                dva[e] = fmaf(pj, gx[e], dva[e]);
-                dka[e] = fmaf(gj, qx[e], dka[e]);
+            for (int x = 0; x < R; ++x) {
+                const float pj = lane_value(p[x], jj), gj = lane_value(ds[x], jj);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    dva[x][e] = fmaf(pj, gx[e], dva[x][e]);
+                    dka[x][e] = fmaf(gj, qx[e], dka[x][e]);
+                }
             }
         }
     }
@@ -227,30 +298,45 @@ __device__ __forceinline__ void kv_sums(const BackwardArgs& a, const float* ks, 
 template <int D>
 __global__ __launch_bounds__(BT) void bwd_kv_kernel(BackwardArgs a) {
     constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) float xs[BW][2][D];
+    __shared__ __attribute__((aligned(16))) float xs[BW][2][RW * D];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t nkeys = (int64_t)a.B * a.Hkv * a.L;
-    const int64_t key = (int64_t)blockIdx.x * BW + wv;     // (b * Hkv + kvh) * L + i
-    if (key >= nkeys) return;
-    const int i = (int)(key % a.L);
-    const int64_t bk = key / a.L;
+    const int64_t ngr = (a.L + RW - 1) / RW;                 // key groups per (b, kv-head)
+    const int64_t grp = (int64_t)blockIdx.x * BW + wv;       // (b * Hkv + kvh) * ngr + key group
+    if (grp >= (int64_t)a.B * a.Hkv * ngr) return;
+    const int64_t bk = grp / ngr;
+    const int ib = (int)(grp % ngr) * RW;                    // keys ib .. ib + nk - 1
+    const int nk = a.L - ib < RW ? (int)(a.L - ib) : RW;
     const int b = (int)(bk / a.Hkv), kvh = (int)(bk % a.Hkv);
+    const int64_t key0 = bk * a.L + ib;
     float* ks = xs[wv][0];
     float* vs = xs[wv][1];
-    stage2<D>(ks, vs, (const __bf16*)a.k + key * D, (const __bf16*)a.v + key * D, lane);
+#pragma unroll
+    for (int x = 0; x < RW; ++x) {
+        const int64_t kx = key0 + (x < nk ? x : nk - 1);
+        stage2<D>(ks + x * D, vs + x * D, (const __bf16*)a.k + kx * D, (const __bf16*)a.v + kx * D, lane);
+    }
     lds_order();
-    // queries i .. i + r - 1 (all of them for i >= s; the first r for a sink)
-    const int64_t tend = (int64_t)i + a.r - 1 < a.L - 1 ? (int64_t)i + a.r - 1 : a.L - 1;
-    float dka[NE], dva[NE];
+    // key ib + x takes the queries ib + x .. ib + x + r - 1 (all of them for
+    // a key >= s; the first r for a sink, whose later ones bwd_sink adds)
+    const int64_t last = (int64_t)ib + nk - 1 + a.r - 1;
+    const int tend = (int)(last < a.L - 1 ? last : a.L - 1);
+    auto ok = [&](int x, int t) { return x < nk && t >= ib + x && (int64_t)t <= (int64_t)ib + x + a.r - 1; };
+    float dka[RW][NE], dva[RW][NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) dka[e] = dva[e] = 0.0f;
-    kv_sums<D>(a, ks, vs, b, kvh, i, (int)(tend - i + 1), lane, dka, dva);
-    float* dk = a.dk + key * D + NE * lane;
-    float* dv = a.dv + key * D + NE * lane;
+    for (int x = 0; x < RW; ++x)
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        dk[e] = dka[e] * a.scale;
-        dv[e] = dva[e];
+        for (int e = 0; e < NE; ++e) dka[x][e] = dva[x][e] = 0.0f;
+    kv_sums<D, RW>(a, ks, vs, b, kvh, ib, tend - ib + 1, lane, ok, dka, dva);
+#pragma unroll
+    for (int x = 0; x < RW; ++x) {
+        if (x >= nk) break;
+        float* dk = a.dk + (key0 + x) * D + NE * lane;
+        float* dv = a.dv + (key0 + x) * D + NE * lane;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            dk[e] = dka[x][e] * a.scale;
+            dv[e] = dva[x][e];
+        }
     }
 }
 
@@ -277,26 +363,27 @@ __global__ __launch_bounds__(BT) void bwd_sink_kernel(BackwardArgs a, int32_t ns
     float* vs = xs[wv][1];
     stage2<D>(ks, vs, (const __bf16*)a.k + key * D, (const __bf16*)a.v + key * D, lane);
     lds_order();
-    float dka[NE], dva[NE];
+    float dka[1][NE], dva[1][NE];
 #pragma unroll
-    for (int e = 0; e < NE; ++e) dka[e] = dva[e] = 0.0f;
-    kv_sums<D>(a, ks, vs, b, kvh, (int)t0, (int)(t1 - t0 + 1), lane, dka, dva);
+    for (int e = 0; e < NE; ++e) dka[0][e] = dva[0][e] = 0.0f;
+    kv_sums<D, 1>(a, ks, vs, b, kvh, (int)t0, (int)(t1 - t0 + 1), lane, [](int, int) { return true; }, dka, dva);
     float* dk = a.dk + key * D + NE * lane;
     float* dv = a.dv + key * D + NE * lane;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
-        atomicAdd(dk + e, dka[e] * a.scale);
-        atomicAdd(dv + e, dva[e]);
+        atomicAdd(dk + e, dka[0][e] * a.scale);
+        atomicAdd(dv + e, dva[0][e]);
     }
 }
 
 template <int D>
 hipError_t launch(const BackwardArgs& a, hipStream_t st) {
-    const int64_t nrows = (int64_t)a.B * a.Hq * a.L, nkeys = (int64_t)a.B * a.Hkv * a.L;
-    hipLaunchKernelGGL((bwd_q_kernel<D>), dim3((unsigned)((nrows + BW - 1) / BW)), dim3(BT), 0, st, a);
+    const int64_t ngr = (a.L + RW - 1) / RW;
+    const int64_t nq = (int64_t)a.B * a.Hq * ngr, nk = (int64_t)a.B * a.Hkv * ngr;
+    hipLaunchKernelGGL((bwd_q_kernel<D>), dim3((unsigned)((nq + BW - 1) / BW)), dim3(BT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_kv_kernel<D>), dim3((unsigned)((nkeys + BW - 1) / BW)), dim3(BT), 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D>), dim3((unsigned)((nk + BW - 1) / BW)), dim3(BT), 0, st, a);
     e = hipGetLastError();
     if (e != hipSuccess || a.s == 0 || a.L <= a.r) return e;
     const int32_t nseg = (int32_t)((a.L - a.r + kSinkSeg - 1) / kSinkSeg);
