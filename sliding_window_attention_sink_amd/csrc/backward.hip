@@ -10,9 +10,11 @@
 //   dQ_t = scale sum_{i in U(t)} dS_ti k_i,   dK_i = scale sum_t dS_ti q_t
 // with dK and dV summed over the q-heads of a kv-head.
 //
-// Three kernels in fp32 vector arithmetic (a plain first backward, not
-// MFMA-tiled); a wave takes eight adjacent rows or keys, so each row a lane
-// reads from memory serves eight dot products:
+// Three kernels on the vector units (a plain first backward, not
+// MFMA-tiled): dot products as bf16 pairs into fp32 (v_dot2c_f32_bf16, the
+// inputs exact), sums in fp32.  A wave takes eight adjacent rows or keys, so
+// each row a lane reads from memory serves eight dot products; the rows
+// staged for the dot products and each chunk's dS (and P) go through LDS:
 //   bwd_q:   per eight query rows, each row's log2-sum-exp over U(t) (one
 //            pass over the union of their keys, lanes over keys), D_t, then
 //            dQ_t (a second pass: lanes score their keys, then lanes over
@@ -32,18 +34,12 @@ namespace swa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BW = 4;               // waves per workgroup, one row or key each
+constexpr int BW = 4;               // waves per workgroup
 constexpr int BT = 64 * BW;
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// lane j's value to every lane (j uniform: a scalar read, no LDS round trip)
-__device__ __forceinline__ float lane_value(float x, int j) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), j));
-}
 
 // This lane's D / 64 consecutive dims of a bf16 row, as fp32.
 template <int D>
@@ -67,41 +63,42 @@ __device__ __forceinline__ float wave_sum(float x) {
 // accesses of one wave complete in order, the clobber keeps the compiler's.
 __device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Stage two bf16 rows of D values into fp32 LDS rows (lanes over dims).
+// Stage two bf16 rows of D values into LDS as they are (bf16 pairs, lanes
+// over pairs).
 template <int D>
-__device__ __forceinline__ void stage2(float* xa, float* xb, const __bf16* ra, const __bf16* rb, int lane) {
-    for (int e = lane; e < D; e += 64) {
-        xa[e] = (float)ra[e];
-        xb[e] = (float)rb[e];
+__device__ __forceinline__ void stage2(uint32_t* xa, uint32_t* xb, const __bf16* ra, const __bf16* rb, int lane) {
+    for (int e = lane; e < D / 2; e += 64) {
+        xa[e] = ((const uint32_t*)ra)[e];
+        xb[e] = ((const uint32_t*)rb)[e];
     }
 }
 
-// R dot products at once: x holds R fp32 rows of D values (LDS, row stride
-// D), row is one bf16 row (global memory), read once for all R.  Elements
-// 0-3 of every 8 go to one accumulator chain and 4-7 to another, so the
-// result does not depend on which operand sits in LDS.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// a[0] b[0] + a[1] b[1] + acc for two bf16 pairs (products exact in fp32)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// R dot products at once: x holds R bf16 rows of D values (LDS, as pairs,
+// row stride D / 2 words), row is one bf16 row (global memory), read once
+// for all R.  Pairs 0-1 of every 4 go to one accumulator chain and 2-3 to
+// another, so the result does not depend on which operand sits in LDS.
 template <int D, int R>
-__device__ __forceinline__ void dot_rows(const float* x, const __bf16* row, float (&out)[R]) {
+__device__ __forceinline__ void dot_rows(const uint32_t* x, const __bf16* row, float (&out)[R]) {
     float c0[R], c1[R];
 #pragma unroll
     for (int q = 0; q < R; ++q) c0[q] = c1[q] = 0.0f;
 #pragma unroll 4
     for (int c = 0; c < D / 8; ++c) {
         const u32x4 w = *(const u32x4*)(row + 8 * c);
-        const float k0 = bf_lo(w[0]), k1 = bf_hi(w[0]), k2 = bf_lo(w[1]), k3 = bf_hi(w[1]);
-        const float k4 = bf_lo(w[2]), k5 = bf_hi(w[2]), k6 = bf_lo(w[3]), k7 = bf_hi(w[3]);
 #pragma unroll
         for (int q = 0; q < R; ++q) {
-            const f32x4 a = *(const f32x4*)(x + q * D + 8 * c);
-            const f32x4 b = *(const f32x4*)(x + q * D + 8 * c + 4);
-            c0[q] = fmaf(a[0], k0, c0[q]);
-            c0[q] = fmaf(a[1], k1, c0[q]);
-            c0[q] = fmaf(a[2], k2, c0[q]);
-            c0[q] = fmaf(a[3], k3, c0[q]);
-            c1[q] = fmaf(b[0], k4, c1[q]);
-            c1[q] = fmaf(b[1], k5, c1[q]);
-            c1[q] = fmaf(b[2], k6, c1[q]);
-            c1[q] = fmaf(b[3], k7, c1[q]);
+            const u32x4 a = *(const u32x4*)(x + q * (D / 2) + 4 * c);
+            c0[q] = dot2(a[0], w[0], c0[q]);
+            c0[q] = dot2(a[1], w[1], c0[q]);
+            c1[q] = dot2(a[2], w[2], c1[q]);
+            c1[q] = dot2(a[3], w[3], c1[q]);
         }
     }
 #pragma unroll
@@ -116,7 +113,8 @@ constexpr int RW = 8;
 template <int D>
 __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
     constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) float xs[BW][2][RW * D];
+    __shared__ __attribute__((aligned(16))) uint32_t xs[BW][2][RW * D / 2];
+    __shared__ __attribute__((aligned(16))) float bc[BW][64 * RW];   // a chunk's dS, [pair][row]
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t ngr = (a.L + RW - 1) / RW;                 // row groups per (b, h)
     const int64_t grp = (int64_t)blockIdx.x * BW + wv;       // (b * Hq + h) * ngr + row group
@@ -130,21 +128,25 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
     const __bf16* kb = (const __bf16*)a.k + ((int64_t)b * a.Hkv + kvh) * a.L * D;
     const __bf16* vb = (const __bf16*)a.v + ((int64_t)b * a.Hkv + kvh) * a.L * D;
     const int64_t row0 = bh * a.L + tb;
-    float* qs = xs[wv][0];
-    float* gs = xs[wv][1];
+    uint32_t* qs = xs[wv][0];
+    uint32_t* gs = xs[wv][1];
     // rows past the end stage row tl again (their results are not stored)
 #pragma unroll
     for (int x = 0; x < RW; ++x) {
         const int64_t rx = row0 + (x < nr ? x : nr - 1);
-        stage2<D>(qs + x * D, gs + x * D, (const __bf16*)a.q + rx * D, (const __bf16*)a.dout + rx * D, lane);
+        stage2<D>(qs + x * (D / 2), gs + x * (D / 2), (const __bf16*)a.q + rx * D, (const __bf16*)a.dout + rx * D,
+                  lane);
     }
     lds_order();
     float Dt[RW];
 #pragma unroll
     for (int x = 0; x < RW; ++x) {
-        const __bf16* orow = (const __bf16*)a.o + (row0 + (x < nr ? x : nr - 1)) * D;
+        const uint32_t* orow = (const uint32_t*)((const __bf16*)a.o + (row0 + (x < nr ? x : nr - 1)) * D);
         float dpart = 0.0f;
-        for (int e = lane; e < D; e += 64) dpart += gs[x * D + e] * (float)orow[e];
+        for (int e = lane; e < D / 2; e += 64) {
+            const uint32_t gw = gs[x * (D / 2) + e], ow = orow[e];
+            dpart += bf_lo(gw) * bf_lo(ow) + bf_hi(gw) * bf_hi(ow);
+        }
         Dt[x] = wave_sum(dpart);
     }
 
@@ -217,18 +219,24 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
             for (int x = 0; x < RW; ++x)
                 if (in_set(x, i)) ds[x] = exp2f(sc[x] * c - lse2[x]) * (dp[x] - Dt[x]);
         }
+        // the chunk's dS through LDS: each key's RW values come back as
+        // broadcast reads in the dims loop
+#pragma unroll
+        for (int x = 0; x < RW; ++x) bc[wv][lane * RW + x] = ds[x];
+        lds_order();
         const int cnt = n - j0 < 64 ? n - j0 : 64;
 #pragma unroll 2
         for (int jj = 0; jj < cnt; ++jj) {
             float kx[NE];
             lane_dims<D>(kb + (int64_t)key_of(j0 + jj) * D, lane, kx);
+            const float* g = &bc[wv][jj * RW];
 #pragma unroll
             for (int x = 0; x < RW; ++x) {
-                const float g = lane_value(ds[x], jj);
 #pragma unroll
-                for (int e = 0; e < NE; ++e) acc[x][e] = fmaf(g, kx[e], acc[x][e]);
+                for (int e = 0; e < NE; ++e) acc[x][e] = fmaf(g[x], kx[e], acc[x][e]);
             }
         }
+        lds_order();
     }
 #pragma unroll
     for (int x = 0; x < RW; ++x) {
@@ -248,8 +256,8 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
 // q-head of the group, for the (key x, query t) pairs with ok(x, t); added
 // into dka, dva (this lane's dims).
 template <int D, int R, class Ok>
-__device__ __forceinline__ void kv_sums(const BackwardArgs& a, const float* ks, const float* vs, int b, int kvh,
-                                        int t0, int nt, int lane, Ok&& ok, float (&dka)[R][D / 64],
+__device__ __forceinline__ void kv_sums(const BackwardArgs& a, const uint32_t* ks, const uint32_t* vs, float* bc,
+                                        int b, int kvh, int t0, int nt, int lane, Ok&& ok, float (&dka)[R][D / 64],
                                         float (&dva)[R][D / 64]) {
     constexpr int NE = D / 64;
     const int G = a.Hq / a.Hkv;
@@ -275,6 +283,14 @@ __device__ __forceinline__ void kv_sums(const BackwardArgs& a, const float* ks, 
                 ds[x] = p[x] * (dp[x] - dd);
             }
         }
+        // the chunk's P and dS through LDS ([pair][P of the R keys, dS of
+        // the R keys]), read back as broadcasts in the dims loop
+#pragma unroll
+        for (int x = 0; x < R; ++x) {
+            bc[lane * 2 * R + x] = p[x];
+            bc[lane * 2 * R + R + x] = ds[x];
+        }
+        lds_order();
         const int cnt = n - j0 < 64 ? n - j0 : 64;
 #pragma unroll 2
         for (int jj = 0; jj < cnt; ++jj) {
@@ -282,23 +298,25 @@ __device__ __forceinline__ void kv_sums(const BackwardArgs& a, const float* ks, 
             float gx[NE], qx[NE];
             lane_dims<D>((const __bf16*)a.dout + qr * D, lane, gx);
             lane_dims<D>((const __bf16*)a.q + qr * D, lane, qx);
+            const float* pj = bc + jj * 2 * R;
 #pragma unroll
             for (int x = 0; x < R; ++x) {
-                const float pj = lane_value(p[x], jj), gj = lane_value(ds[x], jj);
 #pragma unroll
                 for (int e = 0; e < NE; ++e) {
-                    dva[x][e] = fmaf(pj, gx[e], dva[x][e]);
-                    dka[x][e] = fmaf(gj, qx[e], dka[x][e]);
+                    dva[x][e] = fmaf(pj[x], gx[e], dva[x][e]);
+                    dka[x][e] = fmaf(pj[R + x], qx[e], dka[x][e]);
                 }
             }
         }
+        lds_order();
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(BT) void bwd_kv_kernel(BackwardArgs a) {
     constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) float xs[BW][2][RW * D];
+    __shared__ __attribute__((aligned(16))) uint32_t xs[BW][2][RW * D / 2];
+    __shared__ __attribute__((aligned(16))) float bc[BW][64 * 2 * RW];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t ngr = (a.L + RW - 1) / RW;                 // key groups per (b, kv-head)
     const int64_t grp = (int64_t)blockIdx.x * BW + wv;       // (b * Hkv + kvh) * ngr + key group
@@ -308,12 +326,13 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BackwardArgs a) {
     const int nk = a.L - ib < RW ? (int)(a.L - ib) : RW;
     const int b = (int)(bk / a.Hkv), kvh = (int)(bk % a.Hkv);
     const int64_t key0 = bk * a.L + ib;
-    float* ks = xs[wv][0];
-    float* vs = xs[wv][1];
+    uint32_t* ks = xs[wv][0];
+    uint32_t* vs = xs[wv][1];
 #pragma unroll
     for (int x = 0; x < RW; ++x) {
         const int64_t kx = key0 + (x < nk ? x : nk - 1);
-        stage2<D>(ks + x * D, vs + x * D, (const __bf16*)a.k + kx * D, (const __bf16*)a.v + kx * D, lane);
+        stage2<D>(ks + x * (D / 2), vs + x * (D / 2), (const __bf16*)a.k + kx * D, (const __bf16*)a.v + kx * D,
+                  lane);
     }
     lds_order();
     // key ib + x takes the queries ib + x .. ib + x + r - 1 (all of them for
@@ -326,7 +345,7 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BackwardArgs a) {
     for (int x = 0; x < RW; ++x)
 #pragma unroll
         for (int e = 0; e < NE; ++e) dka[x][e] = dva[x][e] = 0.0f;
-    kv_sums<D, RW>(a, ks, vs, b, kvh, ib, tend - ib + 1, lane, ok, dka, dva);
+    kv_sums<D, RW>(a, ks, vs, bc[wv], b, kvh, ib, tend - ib + 1, lane, ok, dka, dva);
 #pragma unroll
     for (int x = 0; x < RW; ++x) {
         if (x >= nk) break;
@@ -345,7 +364,8 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BackwardArgs a) {
 template <int D>
 __global__ __launch_bounds__(BT) void bwd_sink_kernel(BackwardArgs a, int32_t nseg) {
     constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) float xs[BW][2][D];
+    __shared__ __attribute__((aligned(16))) uint32_t xs[BW][2][D / 2];
+    __shared__ __attribute__((aligned(16))) float bc[BW][64 * 2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t nitems = (int64_t)a.B * a.Hkv * a.s * nseg;
     const int64_t item = (int64_t)blockIdx.x * BW + wv;    // ((b * Hkv + kvh) * s + i) * nseg + seg
@@ -359,14 +379,15 @@ __global__ __launch_bounds__(BT) void bwd_sink_kernel(BackwardArgs a, int32_t ns
     if (t0 > a.L - 1) return;
     const int64_t t1 = t0 + kSinkSeg - 1 < a.L - 1 ? t0 + kSinkSeg - 1 : a.L - 1;
     const int64_t key = bk * a.L + i;
-    float* ks = xs[wv][0];
-    float* vs = xs[wv][1];
+    uint32_t* ks = xs[wv][0];
+    uint32_t* vs = xs[wv][1];
     stage2<D>(ks, vs, (const __bf16*)a.k + key * D, (const __bf16*)a.v + key * D, lane);
     lds_order();
     float dka[1][NE], dva[1][NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) dka[0][e] = dva[0][e] = 0.0f;
-    kv_sums<D, 1>(a, ks, vs, b, kvh, (int)t0, (int)(t1 - t0 + 1), lane, [](int, int) { return true; }, dka, dva);
+    kv_sums<D, 1>(a, ks, vs, bc[wv], b, kvh, (int)t0, (int)(t1 - t0 + 1), lane, [](int, int) { return true; }, dka,
+                  dva);
     float* dk = a.dk + key * D + NE * lane;
     float* dv = a.dv + key * D + NE * lane;
 #pragma unroll
