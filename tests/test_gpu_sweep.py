@@ -13,9 +13,12 @@ hand-picked case names.  Three kinds of case:
   range), then fused append + decode steps,
   all with one RoPE base (0 = none); every row is checked against the row
   definition over the whole history;
-* dilated: the dilated-window prefill.
+* dilated: the dilated-window prefill;
+* backward (own draws): dq, dk, dv against the oracle's gradients, the
+  forward's bf16 output as o.
 
-Large cases compare a random sample of rows (first and last rows always in).
+Large forward cases compare a random sample of rows (first and last rows
+always in).
 """
 import numpy as np
 import pytest
@@ -165,3 +168,56 @@ def test_sweep_matches_oracle(gpu, c):
         got = rows_of(o, rows)
     err = max_err(got, ref)
     assert err <= TOL[dt], f"max-abs error {err} over {len(ref)} rows"
+
+
+# ---- backward: its own seeded draws (bf16 inputs, the forward's output as o)
+N_BWD = 24
+
+
+def bwd_case(i: int) -> dict:
+    g = np.random.default_rng(np.random.SeedSequence([0xB4D, i]))
+    Hkv = int(g.choice([1, 2, 4]))
+    grp = int(g.choice([1, 2, 4, 8]))
+    while Hkv * grp > 16:
+        grp //= 2
+    return dict(i=i, kind="backward", dtype="bf16", B=int(g.choice([1, 2])), Hq=Hkv * grp, Hkv=Hkv,
+                d=int(g.choice([64, 128])),
+                L=int(g.choice([int(g.integers(1, 40)), int(g.integers(40, 500)), int(g.integers(500, 1200))],
+                               p=[0.15, 0.5, 0.35])),
+                s=int(g.choice([0, 1, 4, int(g.integers(2, 40)), int(g.integers(40, 140))], p=[0.3, 0.1, 0.3, 0.2, 0.1])),
+                r=int(g.choice([1, int(g.integers(2, 70)), int(g.integers(70, 400)), 4096], p=[0.1, 0.35, 0.4, 0.15])))
+
+
+BWD_CASES = [bwd_case(i) for i in range(N_BWD)]
+
+
+def test_backward_sweep_cases_cover_the_paths():
+    """Dense limit, r = 1, sinks past the window (the sink segments), GQA
+    and both head dims among the drawn backward cases (CPU)."""
+    assert any(c["r"] == 1 for c in BWD_CASES) and any(c["r"] >= c["L"] for c in BWD_CASES)
+    assert any(c["s"] > 0 and c["L"] > c["s"] + c["r"] for c in BWD_CASES)
+    assert any(c["Hq"] // c["Hkv"] >= 4 for c in BWD_CASES) and {64, 128} <= {c["d"] for c in BWD_CASES}
+    assert any(c["L"] % 8 for c in BWD_CASES)   # a partial group of eight rows / keys
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("c", BWD_CASES, ids=["%02d_B%dH%d-%dd%d_L%d_s%d_r%d" % (c["i"], c["B"], c["Hq"], c["Hkv"], c["d"],
+                                                                            c["L"], c["s"], c["r"]) for c in BWD_CASES])
+def test_backward_sweep_matches_oracle(gpu, c):
+    """Gradients within 1e-4 of max(1, largest |gradient|) per tensor (fp32
+    sums of exact products; the bar of the targeted backward tests)."""
+    import sliding_window_attention_sink_amd as swa
+    say("backward sweep", c)
+    B, Hq, Hkv, d, L, s, r = c["B"], c["Hq"], c["Hkv"], c["d"], c["L"], c["s"], c["r"]
+    g = np.random.default_rng(np.random.SeedSequence([0xB4D, c["i"], 1]))
+    q, k, v, do = (si.round_bf16(g.standard_normal((B, H, L, d)).astype(np.float32)) for H in (Hq, Hkv, Hkv, Hq))
+    qd, kd, vd, dod = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
+    od = swa.prefill(qd, kd, vd, s, r)
+    dq, dk, dv = swa.backward(qd, kd, vd, od, dod, s, r)
+    torch.cuda.synchronize()
+    refs = oracle.backward(q, k, v, host(od), do, s, r)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        got = host(got)
+        err = max_err(got, ref)
+        bar = 1e-4 * max(1.0, float(np.abs(ref).max()))
+        assert err <= bar, f"{name}: max-abs error {err} > {bar}"
