@@ -15,10 +15,10 @@
 // inputs exact), sums in fp32.  A wave takes eight adjacent rows or keys, so
 // each row a lane reads from memory serves eight dot products; the rows
 // staged for the dot products and each chunk's dS (and P) go through LDS:
-//   bwd_q:   per eight query rows, each row's log2-sum-exp over U(t) (one
-//            pass over the union of their keys, lanes over keys), D_t, then
-//            dQ_t (a second pass: lanes score their keys, then lanes over
-//            dims add dS_ti k_i); lse and D go to the workspace.
+//   bwd_q:   per eight query rows, D_t, then one pass over the union of
+//            their keys (lanes score keys, then lanes over dims add
+//            dS_ti k_i) with the softmax normalised at the end, as in the
+//            forward's online softmax; lse and D go to the workspace.
 //   bwd_kv:  per eight keys, the queries t = i .. min(L-1, i+r-1) of each
 //            key i from every q-head of its group (for i >= s these are all
 //            of its queries): dK_i, dV_i, stored.
@@ -56,6 +56,12 @@ __device__ __forceinline__ void lane_dims(const __bf16* row, int lane, float (&x
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
     return x;
 }
 
@@ -159,68 +165,52 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
     auto in_set = [&](int x, int i) { return x < nr && i <= tb + x && (i < a.s || i >= tb + x - a.r + 1); };
     const float c = a.scale_log2e;
 
-    // pass 1: log2-sum-exp of each row's scores (per lane, then across lanes)
-    float m[RW], l[RW];
+    // one pass over the keys, the softmax normalised at the end: per row a
+    // running max m (the same in every lane), per lane a partial sum of
+    // exp2(score - m), and dQ accumulated against that m, all rescaled when m
+    // rises (dS_ti l_t = exp2(score - m) (dp - D_t) with l_t the row's sum)
+    float m[RW], lp[RW], acc[RW][NE];
 #pragma unroll
     for (int x = 0; x < RW; ++x) {
         m[x] = -__builtin_inff();
-        l[x] = 0.0f;
+        lp[x] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[x][e] = 0.0f;
     }
     for (int j0 = 0; j0 < n; j0 += 64) {
         const int j = j0 + lane;
+        float v[RW], dp[RW];
+#pragma unroll
+        for (int x = 0; x < RW; ++x) {
+            v[x] = -__builtin_inff();
+            dp[x] = 0.0f;
+        }
         if (j < n) {
             const int i = key_of(j);
             float sc[RW];
             dot_rows<D, RW>(qs, kb + (int64_t)i * D, sc);
-#pragma unroll
-            for (int x = 0; x < RW; ++x) {
-                if (!in_set(x, i)) continue;
-                const float v = sc[x] * c;
-                if (v > m[x]) {
-                    l[x] = l[x] * exp2f(m[x] - v) + 1.0f;
-                    m[x] = v;
-                } else {
-                    l[x] += exp2f(v - m[x]);
-                }
-            }
-        }
-    }
-    float lse2[RW];
-#pragma unroll
-    for (int x = 0; x < RW; ++x) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float m2 = __shfl_xor(m[x], off), l2 = __shfl_xor(l[x], off);
-            const float mm = fmaxf(m[x], m2);
-            l[x] = (m[x] == -__builtin_inff() ? 0.0f : l[x] * exp2f(m[x] - mm)) +
-                   (m2 == -__builtin_inff() ? 0.0f : l2 * exp2f(m2 - mm));
-            m[x] = mm;
-        }
-        lse2[x] = m[x] + log2f(l[x]);
-    }
-
-    // pass 2: dS of each (row, key) (lanes over keys), then dQ (lanes over dims)
-    float acc[RW][NE];
-#pragma unroll
-    for (int x = 0; x < RW; ++x)
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[x][e] = 0.0f;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        const int j = j0 + lane;
-        float ds[RW];
-#pragma unroll
-        for (int x = 0; x < RW; ++x) ds[x] = 0.0f;
-        if (j < n) {
-            const int i = key_of(j);
-            float sc[RW], dp[RW];
-            dot_rows<D, RW>(qs, kb + (int64_t)i * D, sc);
             dot_rows<D, RW>(gs, vb + (int64_t)i * D, dp);
 #pragma unroll
             for (int x = 0; x < RW; ++x)
-                if (in_set(x, i)) ds[x] = exp2f(sc[x] * c - lse2[x]) * (dp[x] - Dt[x]);
+                if (in_set(x, i)) v[x] = sc[x] * c;
         }
-        // the chunk's dS through LDS: each key's RW values come back as
-        // broadcast reads in the dims loop
+        float ds[RW];
+#pragma unroll
+        for (int x = 0; x < RW; ++x) {
+            const float mn = fmaxf(m[x], wave_max(v[x]));
+            if (mn > m[x]) {
+                const float alpha = exp2f(m[x] - mn);     // 0 while m is -inf
+                lp[x] *= alpha;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) acc[x][e] *= alpha;
+                m[x] = mn;
+            }
+            const float p = v[x] == -__builtin_inff() ? 0.0f : exp2f(v[x] - m[x]);
+            lp[x] += p;
+            ds[x] = p * (dp[x] - Dt[x]);
+        }
+        // the chunk's (unnormalised) dS through LDS: each key's RW values
+        // come back as broadcast reads in the dims loop
 #pragma unroll
         for (int x = 0; x < RW; ++x) bc[wv][lane * RW + x] = ds[x];
         lds_order();
@@ -241,11 +231,12 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
 #pragma unroll
     for (int x = 0; x < RW; ++x) {
         if (x >= nr) break;
+        const float l = wave_sum(lp[x]);
         float* dq = a.dq + (row0 + x) * D + NE * lane;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) dq[e] = acc[x][e] * a.scale;
+        for (int e = 0; e < NE; ++e) dq[e] = acc[x][e] * (a.scale / l);
         if (lane == 0) {
-            a.lse2[row0 + x] = lse2[x];
+            a.lse2[row0 + x] = m[x] + log2f(l);
             a.dd[row0 + x] = Dt[x];
         }
     }
