@@ -166,6 +166,25 @@ int swa_decode_step(const swa_desc* desc, const void* q, const void* k_new, cons
                     void* stream);
 
 /*
+ * swa_decode_step without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, kernels, results and errors as swa_decode_step; with more than
+ * one split the per-split partial results go to a static device array of
+ * SWA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs
+ * on until the process ends (the array of the device current at the call).
+ * Calls whose partials need more (B * Hq * n_split * (d + 2) * 4 bytes) are
+ * rejected with SWA_ERR_INVALID_ARG before anything is enqueued.  All calls
+ * on one GPU share that array and it keeps the last call's contents: calls
+ * that overlap on one GPU (other streams, other threads) race on it, so
+ * order them on one stream.  No hipMalloc, hipFree or allocating library
+ * routine is called.
+ */
+#define SWA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int swa_decode_step_noalloc(const swa_desc* desc, const void* q, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, int64_t T, void* o, int32_t n_split, void* stream);
+
+/*
  * Backward of swa_prefill without a cache or RoPE (training): the gradients
  * of the rows O with respect to q, k and v for an upstream gradient dout.
  * The rows are softmax over U(t) of scale * q_t . k_i weighting v_i (the

@@ -10,6 +10,8 @@ of include/swa.h); this package binds it for PyTorch callers:
   * decode(q, kc, vc, T, s, r, ...)    split-K single-query decode
   * decode_step(q, k, v, kc, vc, T, s, r, ...) append token T-1 and decode
                                        it in one launch
+  * decode_step_noalloc(...)           the same without a workspace or any
+                                       allocation (static per-GPU scratch)
   * backward(q, k, v, o, dout, s, r)   gradients of prefill's rows (training)
 
 The low-level same-name wrappers of the C functions are in ``_lib``.
@@ -20,6 +22,7 @@ from .ops import (  # noqa: F401
     cache_append,
     decode,
     decode_step,
+    decode_step_noalloc,
     decode_workspace_bytes,
     make_desc,
     new_cache,

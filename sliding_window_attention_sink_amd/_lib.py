@@ -22,7 +22,7 @@ SWA_BF16 = 1
 # every symbol include/swa.h declares
 EXPORTS = (
     "swa_prefill_workspace_bytes", "swa_prefill", "swa_cache_append", "swa_decode_workspace_bytes",
-    "swa_decode", "swa_decode_step", "swa_decode_default_splits", "swa_prefill_dilated_workspace_bytes",
+    "swa_decode", "swa_decode_step", "swa_decode_step_noalloc", "swa_decode_default_splits", "swa_prefill_dilated_workspace_bytes",
     "swa_prefill_dilated", "swa_backward_workspace_bytes", "swa_backward", "swa_status_str", "swa_last_error",
     "swa_abi_version",
 )
@@ -68,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.swa_decode.restype = ctypes.c_int
     lib.swa_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
     lib.swa_decode_step.restype = ctypes.c_int
+    lib.swa_decode_step_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, i64, vp, i32, vp]
+    lib.swa_decode_step_noalloc.restype = ctypes.c_int
     lib.swa_prefill_dilated_workspace_bytes.argtypes = [dp, i64, i32]
     lib.swa_prefill_dilated_workspace_bytes.restype = sz
     lib.swa_prefill_dilated.argtypes = [dp, i32, vp, vp, vp, vp, i64, vp, sz, vp]
@@ -125,6 +127,14 @@ def swa_decode_step(desc, q, k_new, v_new, k_cache, v_cache, T, o, n_split, work
                     stream) -> int:
     return load().swa_decode_step(ctypes.byref(desc), q, k_new, v_new, k_cache, v_cache, T, o, n_split, workspace,
                                   workspace_bytes, stream)
+
+
+def swa_decode_step_noalloc(desc, q, k_new, v_new, k_cache, v_cache, T, o, n_split, stream) -> int:
+    return load().swa_decode_step_noalloc(ctypes.byref(desc), q, k_new, v_new, k_cache, v_cache, T, o, n_split,
+                                          stream)
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # SWA_NOALLOC_SCRATCH_BYTES of include/swa.h
 
 
 def swa_prefill_dilated_workspace_bytes(desc: SwaDesc, L: int, dilation: int) -> int:

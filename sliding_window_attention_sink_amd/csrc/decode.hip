@@ -34,9 +34,40 @@
 //    current token's slot first writes the token's K/V row there (then
 //    waits for the stores and a barrier), so one launch does the append and
 //    the decode.
+#include <mutex>
+
 #include "swa_internal.h"
 
+// Device scratch of swa_decode_step_noalloc: the per-split partial results
+// (max, sum, unnormalised O) go here instead of a caller-provided workspace.
+// One copy per GPU, held until the process ends.  In host code this name is
+// only a stand-in for the device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device (decode_noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[swa::kNoAllocScratchBytes];
+
 namespace swa {
+
+// The address of this device's scratch array, looked up once per device
+// with that device current.
+hipError_t decode_noalloc_scratch(void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -337,9 +337,10 @@ size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split) {
 namespace {
 
 // swa_decode, and with k_new/v_new swa_decode_step (append fused in).
+// validate_only: check the arguments (the workspace aside) and launch nothing.
 int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void* k_new, const void* v_new,
                 const void* k_cache, const void* v_cache, int64_t T, void* o, int32_t n_split, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool validate_only = false) {
     clear_error();
     int st = check_desc(desc, fn);
     if (st) return st;
@@ -355,11 +356,12 @@ int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void*
     if (T > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: T beyond 2^30", fn);
     if (n_split == 0) n_split = default_splits(desc);
     if (n_split < 1 || n_split > 64) return fail(SWA_ERR_INVALID_ARG, "%s: n_split %d outside 1..64", fn, n_split);
+    if ((int64_t)desc->B * desc->Hkv * n_split > 0x7fffffffLL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
+    if (validate_only) return SWA_OK;
     const size_t need = decode_ws_bytes(desc, n_split);
     if (need > 0 && (st = check_ptr(workspace, fn, "workspace"))) return st;
     if (workspace_bytes < need)
         return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
-    if ((int64_t)desc->B * desc->Hkv * n_split > 0x7fffffffLL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
 
     const int S = desc->s + desc->r;
     int sps = (S + n_split - 1) / n_split;
@@ -405,6 +407,31 @@ int swa_decode_step(const swa_desc* desc, const void* q, const void* k_new, cons
     }
     return decode_impl("swa_decode_step", desc, q, k_new, v_new, k_cache, v_cache, T, o, n_split, workspace,
                        workspace_bytes, stream);
+}
+
+int swa_decode_step_noalloc(const swa_desc* desc, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, int64_t T, void* o, int32_t n_split, void* stream) {
+    static const char* fn = "swa_decode_step_noalloc";
+    clear_error();
+    if (k_new == nullptr || v_new == nullptr) return fail(SWA_ERR_INVALID_ARG, "%s: k_new and v_new are required", fn);
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    const int32_t ns = n_split == 0 ? default_splits(desc) : n_split;
+    if (ns < 1 || ns > 64) return fail(SWA_ERR_INVALID_ARG, "%s: n_split %d outside 1..64", fn, n_split);
+    const size_t need = decode_ws_bytes(desc, ns);
+    if (need > swa::kNoAllocScratchBytes)
+        return fail(SWA_ERR_INVALID_ARG,
+                    "%s: %d splits of B=%d, Hq=%d, d=%d need %zu bytes of scratch, more than the %zu built in "
+                    "(fewer splits or a smaller batch, or swa_decode_step with a workspace)",
+                    fn, ns, desc->B, desc->Hq, desc->d, need, (size_t)swa::kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        // argument checks of decode_impl first, so a rejected call touches no HIP state
+        st = decode_impl(fn, desc, q, k_new, v_new, k_cache, v_cache, T, o, ns, nullptr, 0, nullptr, true);
+        if (st) return st;
+        if ((st = hip_status(swa::decode_noalloc_scratch(&ws), fn))) return st;
+    }
+    return decode_impl(fn, desc, q, k_new, v_new, k_cache, v_cache, T, o, ns, ws, need, stream);
 }
 
 }  // extern "C"

@@ -92,6 +92,11 @@ hipError_t launch_dilate_gather(const DilateArgs& a, const void* src, void* dst,
 hipError_t launch_dilate_scatter(const DilateArgs& a, const void* src, void* dst, int32_t H, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t st);
+
+// Bytes of the static device scratch behind swa_decode_step_noalloc, and
+// its address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+hipError_t decode_noalloc_scratch(void** out);
 hipError_t launch_rope_prepare_bf16(const RopeArgs& a, int d, hipStream_t st);
 
 }  // namespace swa

@@ -191,3 +191,22 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, T, s, r, *, scale=None, rope_
                                n_split, _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                _stream(dev, stream)))
     return out
+
+
+def decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, T, s, r, *, out, scale=None, rope_base=0.0, n_split=0,
+                        stream=None):
+    """decode_step without a workspace: the split partials go to the library's
+    static per-GPU scratch (calls on one GPU must not overlap).  `out` is
+    required, so the call allocates nothing."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    dev = q.device
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale, rope_base=rope_base)
+    _need(k_new, "k_new", (B, Hkv, d), q.dtype, dev)
+    _need(v_new, "v_new", (B, Hkv, d), q.dtype, dev)
+    _need(k_cache, "k_cache", (B, Hkv, s + r, d), q.dtype, dev)
+    _need(v_cache, "v_cache", (B, Hkv, s + r, d), q.dtype, dev)
+    _need(out, "out", q.shape, q.dtype, dev)
+    check(_lib.swa_decode_step_noalloc(desc, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), T,
+                                       _ptr(out), n_split, _stream(dev, stream)))
+    return out

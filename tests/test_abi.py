@@ -185,3 +185,18 @@ def test_last_error_is_per_call():
 def test_ctypes_desc_layout():
     assert ctypes.sizeof(SwaDesc) == 9 * 4
     assert SwaDesc.scale.offset == 28 and SwaDesc.rope_base.offset == 32
+
+
+def test_decode_step_noalloc_rejects_on_host(lib):
+    # partials beyond the static scratch: 64 x 32 heads x 64 splits x 130 floats
+    big = desc(B=64, Hq=32, Hkv=8, s=4, r=4092)
+    st = _lib.swa_decode_step_noalloc(big, A, B_, C, D, E, 100, F, 64, None)
+    assert st == _lib.SWA_ERR_INVALID_ARG and "scratch" in _lib.swa_last_error()
+    assert str(_lib.NOALLOC_SCRATCH_BYTES) in _lib.swa_last_error()
+    # argument errors of swa_decode_step come before any HIP call
+    assert _lib.swa_decode_step_noalloc(desc(), A, None, C, D, E, 100, F, 2, None) == _lib.SWA_ERR_INVALID_ARG
+    assert _lib.swa_decode_step_noalloc(desc(), A, B_, C, D, E, 0, F, 2, None) == _lib.SWA_ERR_INVALID_ARG
+    assert _lib.swa_decode_step_noalloc(desc(), A + 8, B_, C, D, E, 100, F, 2, None) == _lib.SWA_ERR_INVALID_ARG
+    assert _lib.swa_decode_step_noalloc(desc(), A, B_, C, D, E, 100, F, 65, None) == _lib.SWA_ERR_INVALID_ARG
+    assert _lib.swa_decode_step_noalloc(desc(dtype=_lib.SWA_F32), A, B_, C, D, E, 100, F, 2, None) == \
+        _lib.SWA_ERR_UNSUPPORTED
