@@ -66,12 +66,33 @@ typedef struct swa_desc {
 } swa_desc;
 
 /*
- * Bytes of device workspace swa_prefill needs for these arguments.  Zero
- * without RoPE.  With RoPE (rope_base > 0) the keys of the cache and of the
- * chunk and the chunk's queries are rotated once per call into the
- * workspace: (2 * B*Hq*L + B*Hkv*(s + r + L)) * d * 2 bytes, rounded up.
+ * Bytes of device workspace swa_prefill needs for these arguments: 0 (the
+ * prefill kernels use none; kept so callers can size a workspace
+ * generically).
  */
 size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L);
+
+/*
+ * RoPE re-positioning (the StreamingLLM paragraph after
+ * eq:attn-fixed-streaming on the t6page page "滑窗与固定稀疏"): for query t
+ * the keys of U(t), in temporal order, sit at positions 0 .. |U(t)|-1 and the
+ * query at |U(t)|-1.  Rotary scores depend only on the difference of the two
+ * positions, so a window key i sits at its true distance t - i and sink j
+ * at min(t, s+r-1) - j.  The library therefore takes every key rotated ONCE
+ * at its own token's position (with rope_base > 0, the keys given to
+ * swa_prefill, stored by swa_cache_append and read by swa_decode /
+ * swa_decode_step are such keys) and turns the query itself: to t for
+ * window keys, to min(t, s+r-1) for sinks.  Queries are given unrotated.
+ *
+ * swa_rope_keys rotates n key rows per (batch, kv-head) (k, k_rot:
+ * [B, Hkv, n, d], bf16; row i is the token at position pos0 + i) to their
+ * positions: dimension j pairs with j + d/2 and the pair turns by
+ * position * rope_base^(-2j/d) (fp64 angle, fp32 rotation, bf16 result).
+ * k_rot may equal k (in place).  Errors: SWA_ERR_INVALID_ARG (rope_base not
+ * > 0, null/misaligned pointer, n < 1, pos0 < 0), SWA_ERR_UNSUPPORTED (d,
+ * dtype other than bf16), SWA_ERR_HIP.
+ */
+int swa_rope_keys(const swa_desc* desc, const void* k, int64_t n, int64_t pos0, void* k_rot, void* stream);
 
 /*
  * Banded flash-style prefill of L query rows.
@@ -81,12 +102,10 @@ size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L);
  * ([B, Hkv, s + r, d], the rolling cache) hold tokens 0 .. pos0-1 written by
  * swa_cache_append; the cache is read, not written (append the chunk after
  * this call, on the same stream).  pos0 > 0 requires a cache.
- * RoPE (desc->rope_base > 0): keys and values are stored before rotation;
- * for each query the keys of U(t) in temporal order sit at positions
- * 0 .. |U(t)|-1 and the query at |U(t)|-1 (positions re-assigned inside the
- * cache, t6page StreamingLLM paragraph).  Rotation pairs dimension j with
- * j + d/2, angle position * rope_base^(-2j/d).  Needs a workspace of
- * swa_prefill_workspace_bytes() bytes; otherwise workspace may be NULL.
+ * RoPE (desc->rope_base > 0, see swa_rope_keys): k and the cache's keys are
+ * rotated at their tokens' positions, q is not; the kernel rotates each
+ * query to t for the window and to min(t, s+r-1) for the sinks.  workspace
+ * may be NULL (swa_prefill_workspace_bytes() is 0).
  * Errors: SWA_ERR_INVALID_ARG (null or misaligned pointer, L < 1, pos0 < 0,
  * pos0 > 0 without a cache, workspace too small, s < 0, r < 1, Hq % Hkv,
  * scale <= 0), SWA_ERR_UNSUPPORTED (d, dtype, RoPE with fp32), SWA_ERR_HIP.
@@ -139,11 +158,10 @@ size_t swa_decode_workspace_bytes(const swa_desc* desc, int32_t n_split);
  * token first), i.e. U(T-1).  Slot order does not matter to softmax
  * attention over a set, so slots are read in physical order.  Writes
  * o ([B, Hq, d]).  n_split: 0 = the library's choice, else 1 .. 64.
- * With rope_base > 0 the cache holds keys before rotation and q is given
- * before rotation; the keys of U(T-1), in temporal order, are rotated to
- * positions 0 .. |U(T-1)|-1 and the query to |U(T-1)|-1 (the StreamingLLM
- * re-positioning of swa_prefill with a cache; pair j with j + d/2, angle
- * position * rope_base^(-2j/d)).
+ * With rope_base > 0 (up to 8 q-heads per kv-head) the cache holds keys
+ * rotated at their tokens' positions (see swa_rope_keys) and q is given
+ * unrotated; it is turned to T-1 for the window slots and to
+ * min(T-1, s+r-1) for the sink slots (the StreamingLLM re-positioning).
  * Errors: SWA_ERR_INVALID_ARG (null/misaligned pointer, T < 1, workspace too
  * small, n_split out of range), SWA_ERR_UNSUPPORTED (d, dtype other than
  * bf16), SWA_ERR_HIP.
@@ -158,7 +176,7 @@ int swa_decode(const swa_desc* desc, const void* q, const void* k_cache, const v
  * tokens 0 .. T-1.  The result and the cache afterwards equal those of
  * swa_cache_append followed by swa_decode (the token is read from k_new /
  * v_new, and written to its slot, in the same kernel); workspace as for
- * swa_decode.  Errors: those of swa_decode, and SWA_ERR_INVALID_ARG for a
+ * swa_decode.  With rope_base > 0, k_new is rotated at position T-1.  Errors: those of swa_decode, and SWA_ERR_INVALID_ARG for a
  * null or misaligned k_new / v_new.
  */
 int swa_decode_step(const swa_desc* desc, const void* q, const void* k_new, const void* v_new, void* k_cache,

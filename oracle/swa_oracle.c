@@ -215,13 +215,19 @@ int swa_oracle_attend_set(const float* q, const float* keys, const float* vals, 
     return ORACLE_OK;
 }
 
-/* The rotation alone, exposed so tests can pin it to closed forms. */
+/* The rotation alone, exposed so tests can pin it to closed forms.  One
+ * position, so the angles are formed directly (the same cos(p * theta_j) and
+ * sin(p * theta_j) a table entry holds), for positions of any size. */
 int swa_oracle_rope(const double* x, double* y, int64_t d, int64_t pos, double base) {
     if (!x || !y || d < 2 || (d % 2) || !(base > 0) || pos < 0) return ORACLE_EINVAL;
-    rope_table T;
-    if (rope_table_init(&T, pos + 1, d, base) != ORACLE_OK) return ORACLE_ENOMEM;
-    rope_rotate(&T, x, y, pos);
-    rope_table_free(&T);
+    int64_t h = d / 2;
+    for (int64_t j = 0; j < h; ++j) {
+        double theta = pow(base, -2.0 * (double)j / (double)d);
+        double c = cos((double)pos * theta), sn = sin((double)pos * theta);
+        double x0 = x[j], x1 = x[j + h];
+        y[j] = x0 * c - x1 * sn;
+        y[j + h] = x0 * sn + x1 * c;
+    }
     return ORACLE_OK;
 }
 

@@ -21,7 +21,7 @@ SWA_BF16 = 1
 
 # every symbol include/swa.h declares
 EXPORTS = (
-    "swa_prefill_workspace_bytes", "swa_prefill", "swa_cache_append", "swa_decode_workspace_bytes",
+    "swa_prefill_workspace_bytes", "swa_rope_keys", "swa_prefill", "swa_cache_append", "swa_decode_workspace_bytes",
     "swa_decode", "swa_decode_step", "swa_decode_step_noalloc", "swa_decode_default_splits", "swa_prefill_dilated_workspace_bytes",
     "swa_prefill_dilated", "swa_backward_workspace_bytes", "swa_backward", "swa_status_str", "swa_last_error",
     "swa_abi_version",
@@ -58,6 +58,8 @@ def load() -> ctypes.CDLL:
     dp = ctypes.POINTER(SwaDesc)
     lib.swa_prefill_workspace_bytes.argtypes = [dp, i64]
     lib.swa_prefill_workspace_bytes.restype = sz
+    lib.swa_rope_keys.argtypes = [dp, vp, i64, i64, vp, vp]
+    lib.swa_rope_keys.restype = ctypes.c_int
     lib.swa_prefill.argtypes = [dp, vp, vp, vp, vp, i64, vp, vp, i64, vp, sz, vp]
     lib.swa_prefill.restype = ctypes.c_int
     lib.swa_cache_append.argtypes = [dp, vp, vp, i64, i64, vp, vp, vp]
@@ -99,6 +101,10 @@ def check(status: int) -> None:
 # ---- same-name wrappers over raw addresses (ints or None) -----------------
 def swa_prefill_workspace_bytes(desc: SwaDesc, L: int) -> int:
     return load().swa_prefill_workspace_bytes(ctypes.byref(desc), L)
+
+
+def swa_rope_keys(desc, k, n, pos0, k_rot, stream) -> int:
+    return load().swa_rope_keys(ctypes.byref(desc), k, n, pos0, k_rot, stream)
 
 
 def swa_prefill(desc, q, k, v, o, L, k_cache, v_cache, pos0, workspace, workspace_bytes, stream) -> int:

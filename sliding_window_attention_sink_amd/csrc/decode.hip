@@ -22,20 +22,22 @@
 //    and split; a second kernel merges the splits and normalises.  With one
 //    split (enough (batch, kv-head) units to fill the chip) the workgroup
 //    writes the normalised output itself and the second kernel is skipped.
-//  * RoPE re-positioning (rope_log2_base > 0): the cache holds keys before
-//    rotation and U(T-1) sits at consecutive positions in temporal order, the
-//    query at the last (the StreamingLLM paragraph after
-//    eq:attn-fixed-streaming on the t6page page): the query is rotated once
-//    to min(T-1, s+r-1) and every key, as it arrives in registers, to its
-//    rank (sinks j -> j; a window token p -> s + p - max(s, T-r)).  Angles
-//    are reduced in fp64, then turned by v_sin/v_cos in fp32; dimension j
-//    pairs with j + d/2 and turns by rank * base^(-2j/d).
+//  * RoPE re-positioning (rope_rr > 0): U(T-1) sits at consecutive
+//    positions in temporal order, the query at the last (the StreamingLLM
+//    paragraph after eq:attn-fixed-streaming on the t6page page).  Window
+//    keys then sit at their true distance from the query and sink j at
+//    min(T-1, s+r-1) - j, so the cache holds every key rotated once at its
+//    token's position (swa_rope_keys) and only the query turns: at T-1
+//    for window slots, at min(T-1, s+r-1) for sink slots.  The two rotated
+//    copies of each q-head take two of the 16 MFMA query columns, so one
+//    product scores both; sink slots take the second column's score.
 //  * fused step (kn/vn given): the workgroup whose slot range holds the
 //    current token's slot first writes the token's K/V row there (then
 //    waits for the stores and a barrier), so one launch does the append and
 //    the decode.
 #include <mutex>
 
+#include "rope_common.h"
 #include "swa_internal.h"
 
 // Device scratch of swa_decode_step_noalloc: the per-split partial results
@@ -99,29 +101,6 @@ struct DecodeSmem {
 
 __device__ __forceinline__ int vswz(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
 
-// Rotate the eight dimension pairs (lo[e], hi[e]) (dims j and j + d/2, bf16)
-// by pos * fr[e] revolutions.
-__device__ __forceinline__ void rope_rot8(u32x4& lo, u32x4& hi, const double* fr, double pos) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        uint32_t rl = 0, rh = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const double rv = pos * fr[2 * w + h];
-            const float x = (float)(rv - __builtin_floor(rv));
-            const float c = __builtin_amdgcn_cosf(x), sn = __builtin_amdgcn_sinf(x);
-            const float x0 = __builtin_bit_cast(float, (lo[w] >> (16 * h)) << 16);
-            const float x1 = __builtin_bit_cast(float, (hi[w] >> (16 * h)) << 16);
-            const uint32_t y0 = __builtin_bit_cast(uint16_t, (__bf16)(x0 * c - x1 * sn));
-            const uint32_t y1 = __builtin_bit_cast(uint16_t, (__bf16)(x0 * sn + x1 * c));
-            rl |= y0 << (16 * h);
-            rh |= y1 << (16 * h);
-        }
-        lo[w] = rl;
-        hi[w] = rh;
-    }
-}
-
 template <int D, bool ROPE>
 __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     __shared__ DecodeSmem<D> sm;
@@ -155,7 +134,8 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
             const int c = lane % CH;
             const bool is_v = lane >= CH;
             const u32x4* src = (const u32x4*)((const __bf16*)(is_v ? a.vn : a.kn) + (size_t)bh * D);
-            ((u32x4*)((__bf16*)(is_v ? a.vc : a.kc) + ((size_t)bh * S + a.j_new) * D))[c] = src[c];
+            u32x4* dst = (u32x4*)((__bf16*)(is_v ? a.vc : a.kc) + ((size_t)bh * S + a.j_new) * D);
+            dst[c] = src[c];
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores have completed
         __syncthreads();
@@ -174,40 +154,24 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
         return first <= T - 1;
     };
 
-    // RoPE: revolutions per position of this lane's first-half dims
-    // 32 ks + 8 g + e (ks < HK); the partner dims sit at k-step ks + HK
+    // Q^T operand: column col = q-head kvh*G + col (zero past the group);
+    // with RoPE columns G .. 2G-1 hold the same heads rotated for the sinks
     constexpr int HK = KSTEPS / 2;
     constexpr bool rope = ROPE;
-    double frev[HK * 8];
-    if (rope) {
-#pragma unroll
-        for (int ks = 0; ks < HK; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                frev[8 * ks + e] = exp2(-(2.0 * (32 * ks + 8 * g + e) / D) * a.rope_log2_base) * 0.15915494309189535;
-    }
-    // position of the key in slot j among U(T-1) in temporal order
-    const int64_t win_lo = (T - a.r) > a.s ? (T - a.r) : (int64_t)a.s;
-    auto rank_of = [&](int j) -> double {
-        if (j < a.s) return (double)j;
-        const uint32_t q = (uint32_t)(j - a.s);
-        const int64_t p = (T - 1) - (int64_t)(((uint32_t)(T - 1) - q) % (uint32_t)a.r);
-        return (double)(a.s + p - win_lo);
-    };
-
-    // Q^T operand: column col = head kvh*G + col (zero past the group)
     bf16x8 qreg[KSTEPS];
     {
-        const bool qv = col < G;
-        const __bf16* qrow = (const __bf16*)a.q + ((size_t)b * a.Hq + kvh * G + (qv ? col : 0)) * D;
+        const bool qband = col < G;
+        const bool qsink = rope && col >= G && col < 2 * G;
+        const int head = qband ? col : (qsink ? col - G : 0);
+        const __bf16* qrow = (const __bf16*)a.q + ((size_t)b * a.Hq + kvh * G + head) * D;
         u32x4 x[KSTEPS];
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
-            x[ks] = qv ? *(const u32x4*)(qrow + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+            x[ks] = (qband || qsink) ? *(const u32x4*)(qrow + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
         if (rope) {
-            const double qpos = (double)(T - 1 < (int64_t)S - 1 ? T - 1 : (int64_t)S - 1);
+            const int64_t qpos = qband ? T - 1 : (T - 1 < (int64_t)S - 1 ? T - 1 : (int64_t)S - 1);
 #pragma unroll
-            for (int ks = 0; ks < HK; ++ks) rope_rot8(x[ks], x[ks + HK], frev + 8 * ks, qpos);
+            for (int ks = 0; ks < HK; ++ks) rope::rot_chunk_pair(x[ks], x[ks + HK], 32 * ks + 8 * g, (double)qpos, a.rope_rr);
         }
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, x[ks]);
@@ -220,7 +184,8 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     const float c = a.scale_log2e;
 
     // one step's K (MFMA operand order) and V rows in registers; without
-    // RoPE two such buffers keep two steps of loads in flight per wave
+    // RoPE two such buffers keep two steps of loads in flight per wave (with
+    // RoPE the sink-score exchange needs the registers of the second)
     struct StepRegs {
         u32x4 k[2][KSTEPS];
         u32x4 v[KPL];
@@ -253,14 +218,6 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
         auto& kr = R.k;
         auto& vr = R.v;
         const int kb = j0 + st * KW;
-        if (rope) {
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const double pos = rank_of(kb + dec_key(bb, col));
-#pragma unroll
-                for (int ks = 0; ks < HK; ++ks) rope_rot8(kr[bb][ks], kr[bb][ks + HK], frev + 8 * ks, pos);
-            }
-        }
         f32x4 sacc[2];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
@@ -290,6 +247,16 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
         }
         if (st + DEPTH < st1) load(R, st + DEPTH);
 
+        if (rope && kb < a.s) {
+            // sink slots: head col scores with its sink-rotated copy, column col + G
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sk = __shfl(sacc[bb][i], lane + G);
+                    if (col < G && kb + 8 * g + 4 * bb + i < a.s) sacc[bb][i] = sk;
+                }
+        }
         const bool step_full = all_valid && kb + KW <= j1;
         if (!step_full) {
 #pragma unroll
@@ -407,7 +374,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
     const unsigned nblk = (unsigned)a.B * a.Hkv * a.n_split;
-    if (a.rope_log2_base > 0.0)
+    if (a.rope_rr > 0.0)
         hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(nblk), dim3(NT), 0, st, a);
     else
         hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(nblk), dim3(NT), 0, st, a);

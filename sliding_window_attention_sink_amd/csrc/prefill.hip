@@ -206,11 +206,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
         const int lo_any = P.band_lo > t0 - r + 1 ? P.band_lo : t0 - r + 1;
         auto loadable = [&](int p) __attribute__((always_inline)) { return p <= t1 && (p < P.sink_hi || p >= lo_any); };
 
-        const int want_q = (P.use_qs && a.qs != a.q) ? 1 : 0;
-        if (want_q != q_loaded) {
-            const T* qsrc = (const T*)(want_q ? a.qs : a.q) + qoff;
-            TL::load_q(qreg, qsrc, my_valid, g);
-            q_loaded = want_q;
+        if (q_loaded < 0) {
+            TL::load_q(qreg, (const T*)a.q + qoff, my_valid, g);
+            q_loaded = 0;
         }
 
         // Tile-uniform choice of the load path: rows that every query of the

@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "prefill_common.h"
+#include "rope_common.h"
 
 namespace swa {
 namespace {
@@ -121,6 +122,15 @@ struct PP {
 #pragma unroll
         for (int ks = 0; ks < QK_STEPS; ++ks)
             Q.q[ks] = valid ? *(const u32x4*)(row + 8 * (2 * ks + g)) : u32x4{0, 0, 0, 0};
+    }
+
+    // RoPE: rotate the lane's query row to position pos.  Chunk 2 ks + g
+    // (dims 16 ks + 8 g ..) pairs with chunk 2 (ks + QK_STEPS/2) + g, d/2
+    // dims further, which the same lane holds.
+    static __device__ __forceinline__ void rope_q(QRegs& Q, int pos, double rr, int g) {
+#pragma unroll
+        for (int ks = 0; ks < QK_STEPS / 2; ++ks)
+            rope::rot_chunk_pair(Q.q[ks], Q.q[ks + QK_STEPS / 2], 16 * ks + 8 * g, (double)pos, rr);
     }
 
     // Byte offset in a V tile of this lane's transposing reads for d-block db.
@@ -522,7 +532,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
 
     // ---- per-wave state
     typename T::QRegs qr;
-    int q_loaded = -1;
+    int q_loaded = -1, q_raw = -1;
     f32x16 oacc[T::NDB];
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db) oacc[db] = f32x16{};
@@ -535,15 +545,26 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     f32x16 sacc0 = {}, sacc1 = {};     // scores of a tile, from its C to its X cluster
     bf16x8 pk[4];                      // P of a tile, from its X cluster to the next C
 
-    // The queries tile v is scored with (RoPE: the sink phase uses queries
-    // rotated to min(t, s+r-1)); reloaded only when the phase changes, and
-    // waited for here so no later instruction waits on it.
+    // The queries tile v is scored with.  With RoPE the band phase takes the
+    // query rotated to t and the sink phase the query rotated to
+    // min(t, s+r-1) (keys are stored rotated at their own positions); the
+    // rotated copy is made when the phase changes, from a fresh read of the
+    // row (waited for here so no later instruction waits on it), or from the
+    // row the prologue read (q_raw: which copy it is meant for).
+    const bool rope = a.rope_rr > 0.0;
     auto ensure_q = [&](int v) __attribute__((always_inline)) {
-        const int want_q = (phase_of(v).use_qs && a.qs != a.q) ? 1 : 0;
+        const int want_q = (rope && phase_of(v).use_qs) ? 1 : 0;
         if (want_q != q_loaded) {
-            T::load_q(qr, (const __bf16*)(want_q ? a.qs : a.q) + qoff, my_valid, g);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            if (q_raw != want_q) {
+                T::load_q(qr, (const __bf16*)a.q + qoff, my_valid, g);
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            }
+            if (rope) {
+                const int cap = s + r - 1;
+                T::rope_q(qr, want_q ? (my_t < cap ? my_t : cap) : my_t, a.rope_rr, g);
+            }
             q_loaded = want_q;
+            q_raw = -1;
         }
     };
 
@@ -656,9 +677,11 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     if (nv > 0) {
         // the queries of tile 0 travel with the first tiles' loads
         if (wave_active) {
-            const int want_q = (phase_of(0).use_qs && a.qs != a.q) ? 1 : 0;
-            T::load_q(qr, (const __bf16*)(want_q ? a.qs : a.q) + qoff, my_valid, g);
-            q_loaded = want_q;
+            T::load_q(qr, (const __bf16*)a.q + qoff, my_valid, g);
+            if (a.rope_rr > 0.0)
+                q_raw = phase_of(0).use_qs ? 1 : 0;   // rotated in ensure_q, after the prologue's wait
+            else
+                q_loaded = 0;
         }
         if (grp == 0) {
             issue(K_, 0, 0);

@@ -69,23 +69,8 @@ int hip_status(hipError_t e, const char* fn) {
 
 size_t elem_bytes(const swa_desc* d) { return d->dtype == SWA_BF16 ? 2 : 4; }
 
-struct RopeLayout {
-    size_t qb, qs, knr, kcr, total;
-};
-
-RopeLayout rope_layout(const swa_desc* d, int64_t L) {
-    RopeLayout r{};
-    const size_t row = (size_t)d->d * 2;
-    const size_t nq = (size_t)d->B * d->Hq * L * row;
-    const size_t nk = (size_t)d->B * d->Hkv * L * row;
-    const size_t nc = (size_t)d->B * d->Hkv * (d->s + d->r) * row;
-    r.qb = 0;
-    r.qs = round_up(r.qb + nq, 256);
-    r.knr = round_up(r.qs + nq, 256);
-    r.kcr = round_up(r.knr + nk, 256);
-    r.total = round_up(r.kcr + nc, 256);
-    return r;
-}
+// Rotation frequencies theta_j = base^(-2j/d) = rope_rr(desc)^j.
+double rope_rr(const swa_desc* d) { return std::pow((double)d->rope_base, -2.0 / (double)d->d); }
 
 // Splits per (batch, kv-head) unit: enough workgroups for two per compute
 // unit (512 on 256 CUs), each over at least 256 slots; one split when the
@@ -152,8 +137,7 @@ const char* swa_status_str(int status) {
 
 size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L) {
     if (check_desc(desc, "swa_prefill_workspace_bytes") != SWA_OK || L < 1) return 0;
-    if (!(desc->rope_base > 0.0f)) return 0;
-    return rope_layout(desc, L).total;
+    return 0;
 }
 
 int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
@@ -175,14 +159,9 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
     } else if (pos0 != 0) {
         return fail(SWA_ERR_INVALID_ARG, "%s: pos0 > 0 needs the rolling cache", fn);
     }
+    (void)workspace;
+    (void)workspace_bytes;
     const bool rope = desc->rope_base > 0.0f;
-    RopeLayout rl{};
-    if (rope) {
-        rl = rope_layout(desc, L);
-        if ((st = check_ptr(workspace, fn, "workspace"))) return st;
-        if (workspace_bytes < rl.total)
-            return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, rl.total);
-    }
     const bool bf16 = desc->dtype == SWA_BF16;
     const int64_t rows_per_block =
         bf16 ? swa::prefill_bf16_rows_per_block(desc->Hq, desc->Hkv) : swa::kPrefillF32RowsPerBlock;
@@ -193,7 +172,6 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     swa::PrefillArgs a{};
     a.q = q;
-    a.qs = q;
     a.kn = k;
     a.vn = v;
     a.kc = has_cache ? k_cache : nullptr;
@@ -212,29 +190,9 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
     a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
 
     if (rope) {
-        char* ws = static_cast<char*>(workspace);
-        swa::RopeArgs ra{};
-        ra.q = q;
-        ra.kn = k;
-        ra.kc = has_cache ? k_cache : nullptr;
-        ra.qb = ws + rl.qb;
-        ra.qsk = ws + rl.qs;
-        ra.knr = ws + rl.knr;
-        ra.kcr = ws + rl.kcr;
-        ra.L = L;
-        ra.pos0 = pos0;
-        ra.B = desc->B;
-        ra.Hq = desc->Hq;
-        ra.Hkv = desc->Hkv;
-        ra.s = desc->s;
-        ra.r = desc->r;
-        ra.base = desc->rope_base;
-        if ((st = hip_status(swa::launch_rope_prepare_bf16(ra, desc->d, hs), fn))) return st;
-        a.q = ra.qb;
-        a.qs = ra.qsk;
-        a.kn = ra.knr;
-        a.kc = has_cache ? ra.kcr : nullptr;
+        // the keys (own and cached) come rotated; the kernel turns the queries
         a.merge_sink = 0;
+        a.rope_rr = rope_rr(desc);
     }
     hipError_t e = bf16 ? swa::launch_prefill_bf16(a, desc->d, hs) : swa::launch_prefill_f32(a, desc->d, hs);
     return hip_status(e, fn);
@@ -271,6 +229,26 @@ int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new,
     a.d = desc->d;
     a.elem_bytes = (int32_t)elem_bytes(desc);
     return hip_status(swa::launch_append(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int swa_rope_keys(const swa_desc* desc, const void* k, int64_t n, int64_t pos0, void* k_rot, void* stream) {
+    static const char* fn = "swa_rope_keys";
+    clear_error();
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    if (!(desc->rope_base > 0.0f)) return fail(SWA_ERR_INVALID_ARG, "%s: rope_base must be > 0", fn);
+    if ((st = check_ptr(k, fn, "k")) || (st = check_ptr(k_rot, fn, "k_rot"))) return st;
+    if (n < 1) return fail(SWA_ERR_INVALID_ARG, "%s: n must be >= 1 (got %lld)", fn, (long long)n);
+    if (pos0 < 0) return fail(SWA_ERR_INVALID_ARG, "%s: pos0 must be >= 0", fn);
+    if (pos0 + n > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
+    swa::RopeKeysArgs a{};
+    a.k = k;
+    a.kr = k_rot;
+    a.rows = (int64_t)desc->B * desc->Hkv * n;
+    a.n = n;
+    a.pos0 = pos0;
+    a.rope_rr = rope_rr(desc);
+    return hip_status(swa::launch_rope_keys_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 size_t swa_prefill_dilated_workspace_bytes(const swa_desc* desc, int64_t L, int32_t dilation) {
@@ -347,6 +325,8 @@ int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void*
     if (desc->dtype != SWA_BF16) return fail(SWA_ERR_UNSUPPORTED, "%s: decode is built for bf16 only", fn);
     if (desc->Hq / desc->Hkv > 16)
         return fail(SWA_ERR_UNSUPPORTED, "%s: more than 16 q-heads per kv-head", fn);
+    if (desc->rope_base > 0.0f && desc->Hq / desc->Hkv > 8)
+        return fail(SWA_ERR_UNSUPPORTED, "%s: RoPE decode is built for up to 8 q-heads per kv-head", fn);
     if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k_cache, fn, "k_cache")) ||
         (st = check_ptr(v_cache, fn, "v_cache")) || (st = check_ptr(o, fn, "o")))
         return st;
@@ -384,7 +364,7 @@ int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void*
     a.n_split = n_split;
     a.slots_per_split = sps;
     a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
-    a.rope_log2_base = desc->rope_base > 0.0f ? std::log2((double)desc->rope_base) : 0.0;
+    a.rope_rr = desc->rope_base > 0.0f ? rope_rr(desc) : 0.0;
     return hip_status(swa::launch_decode_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 

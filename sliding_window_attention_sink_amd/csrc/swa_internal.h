@@ -15,8 +15,7 @@ constexpr int kPrefillF32RowsPerBlock = 128;
 //   kn/vn + (p - pos0) * d otherwise (the call's own tokens)
 // per (b, kv-head); q/o per (b, q-head) hold L rows.
 struct PrefillArgs {
-    const void* q;      // band queries (rotated to t when RoPE)
-    const void* qs;     // sink queries (rotated to min(t, s+r-1) when RoPE; == q otherwise)
+    const void* q;      // queries (before rotation with RoPE)
     const void* kn;
     const void* vn;
     const void* kc;
@@ -29,6 +28,10 @@ struct PrefillArgs {
     int32_t merge_sink; // 1: sinks may share tiles with the band (same queries for both)
     int32_t pair_mode;  // bf16 kernel: workgroup = two q-heads of one kv-head (else 256 rows of one head)
     float scale_log2e;  // scale * log2(e)
+    // RoPE (rope_rr > 0): every key, own and cached, comes rotated at its
+    // token's position; the kernel rotates the queries, at t for window keys
+    // and at min(t, s+r-1) for sinks.  rope_rr = base^(-2/d).
+    double rope_rr;
 };
 
 struct AppendArgs {
@@ -53,25 +56,20 @@ struct DecodeArgs {
     const void* vn;     // same for V
     int64_t T;          // tokens in the cache including the current one
     int32_t j_new;      // cache slot of token T-1 with kn/vn, else -1
-    double rope_log2_base;  // log2(RoPE base), 0 = no RoPE
+    double rope_rr;     // RoPE: base^(-2/d) (cache keys stored rotated at their position); 0 = no RoPE
     int32_t B, Hq, Hkv, s, r;
     int32_t n_split;
     int32_t slots_per_split;
     float scale_log2e;
 };
 
-struct RopeArgs {
-    const void* q;      // [B, Hq, L, d] chunk queries (pre-rotation)
-    const void* kn;     // [B, Hkv, L, d] chunk keys (pre-rotation)
-    const void* kc;     // [B, Hkv, s + r, d] cache keys (pre-rotation) or null
-    void* qb;           // out: queries rotated to t
-    void* qsk;          // out: queries rotated to min(t, s + r - 1)
-    void* knr;          // out: chunk keys rotated to their position
-    void* kcr;          // out: cache keys rotated to their token's position (valid slots)
-    int64_t L;
-    int64_t pos0;
-    int32_t B, Hq, Hkv, s, r;
-    float base;
+// Rows [rows, d] of keys for positions pos0 + (row mod n) (the rows of
+// each (batch, kv-head) hold tokens pos0 .. pos0+n-1), rotated into kr.
+struct RopeKeysArgs {
+    const void* k;
+    void* kr;
+    int64_t rows, n, pos0;
+    double rope_rr;     // base^(-2/d)
 };
 
 // Query rows per workgroup of the bf16 prefill kernel for this head layout.
@@ -97,6 +95,6 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t st);
 // its address on the current device (looked up once per device).
 constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
 hipError_t decode_noalloc_scratch(void** out);
-hipError_t launch_rope_prepare_bf16(const RopeArgs& a, int d, hipStream_t st);
+hipError_t launch_rope_keys_bf16(const RopeKeysArgs& a, int d, hipStream_t st);
 
 }  // namespace swa

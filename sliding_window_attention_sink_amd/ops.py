@@ -50,12 +50,27 @@ def prefill_workspace_bytes(desc: SwaDesc, L: int) -> int:
     return _lib.swa_prefill_workspace_bytes(desc, L)
 
 
+def rope_keys(k, pos0, base, *, out=None, stream=None):
+    """Keys k [B,Hkv,n,d] (bf16; row i = position pos0 + i) rotated at their
+    positions: the form prefill, cache_append and decode take with RoPE."""
+    B, Hkv, n, d = k.shape
+    dev = k.device
+    desc = make_desc(B, Hkv, Hkv, d, 0, 1, k.dtype, rope_base=base)
+    if out is None:
+        out = torch.empty_like(k)
+    _need(out, "out", k.shape, k.dtype, dev)
+    check(_lib.swa_rope_keys(desc, _ptr(k), n, pos0, _ptr(out), _stream(dev, stream)))
+    return out
+
+
 def prefill(q, k, v, s, r, *, scale=None, rope_base=0.0, k_cache=None, v_cache=None, pos0=0, out=None,
             workspace=None, stream=None):
     """O = sliding-window attention with sinks over q [B,Hq,L,d], k/v [B,Hkv,L,d].
 
     With k_cache/v_cache ([B,Hkv,s+r,d]) rows are positions pos0.. and keys
-    before pos0 come from the cache (chunked prefill).
+    before pos0 come from the cache (chunked prefill).  With rope_base > 0 the
+    keys (k and the cache's) are rotated at their positions (rope_keys) and q
+    is not.
     """
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]

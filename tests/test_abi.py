@@ -83,15 +83,30 @@ def test_prefill_rejects_args(lib):
     assert "desc is NULL" in _lib.swa_last_error()
 
 
-def test_prefill_rope_workspace():
-    d_ = desc(rope_base=10000.0)
-    need = _lib.swa_prefill_workspace_bytes(d_, 100)
-    row = 128 * 2
-    assert need >= (2 * 1 * 4 * 100 + 1 * 2 * (4 + 28 + 100)) * row
-    assert prefill(d_, ws=None) == -1 and "workspace is NULL" in _lib.swa_last_error()
-    assert prefill(d_, ws=W, wsb=need - 1) == -1 and "needed" in _lib.swa_last_error()
+def test_prefill_needs_no_workspace():
+    # keys come rotated (swa_rope_keys), so no call needs a workspace
+    assert _lib.swa_prefill_workspace_bytes(desc(rope_base=10000.0), 100) == 0
     assert _lib.swa_prefill_workspace_bytes(desc(), 100) == 0
     assert _lib.swa_prefill_workspace_bytes(desc(r=0), 100) == 0
+
+
+def test_rope_keys_rejects():
+    d_ = desc(rope_base=10000.0)
+    assert _lib.swa_rope_keys(desc(), A, 4, 0, B_, None) == -1 and "rope_base" in _lib.swa_last_error()
+    assert _lib.swa_rope_keys(d_, None, 4, 0, B_, None) == -1 and "k is NULL" in _lib.swa_last_error()
+    assert _lib.swa_rope_keys(d_, A, 4, 0, B_ + 8, None) == -1 and "aligned" in _lib.swa_last_error()
+    assert _lib.swa_rope_keys(d_, A, 0, 0, B_, None) == -1 and "n must be" in _lib.swa_last_error()
+    assert _lib.swa_rope_keys(d_, A, 4, -1, B_, None) == -1 and "pos0" in _lib.swa_last_error()
+    assert _lib.swa_rope_keys(d_, A, 4, (1 << 30) - 2, B_, None) == -1
+    assert _lib.swa_rope_keys(desc(rope_base=1e4, d=80), A, 4, 0, B_, None) == -2
+    assert _lib.swa_rope_keys(desc(rope_base=1e4, dtype=_lib.SWA_F32), A, 4, 0, B_, None) == -2
+
+
+def test_rope_decode_group_limit():
+    # the band and sink copies of a kv-head's q-heads share 16 MFMA columns
+    d_ = desc(Hq=16, Hkv=1, rope_base=1e4)
+    assert _lib.swa_decode(d_, A, B_, C, 100, D, 1, None, 0, None) == -2
+    assert "8 q-heads" in _lib.swa_last_error()
 
 
 def test_append_rejects():

@@ -38,27 +38,54 @@ def test_main_workload_flops():
     assert abs(bench.prefill_flops(w) - 4.124e11) / 4.124e11 < 1e-3
 
 
-def _note(tmp_path, body, sha):
-    p = tmp_path / "note.md"
+def test_main_step_flops():
+    """The main step credits the 32 chunks' pairs: 8.659e12 flops for
+    H = 32, d = 128, L = 131072, s + r = 4096 (528,484,352 pairs per head);
+    chunk 0 (no cache) has half a full chunk's pairs plus the growing rows."""
+    w = si.WORKLOADS[5]
+    assert bench.MAIN_WID == 5
+    assert bench.key_count_sum(w.L, w.s, w.r) == 528484352
+    assert bench.chunk_flops(w, 0, w.L) == 4.0 * 128 * 528484352 * 32
+    assert abs(bench.chunk_flops(w, 0, w.L) - 8.659e12) / 8.659e12 < 1e-3
+    parts = sum(bench.chunk_flops(w, p, p + w.chunk) for p in range(0, w.L, w.chunk))
+    assert parts == bench.chunk_flops(w, 0, w.L)
+    assert bench.chunk_flops(w, 4096, 8192) == 4.0 * 128 * 4096 * 4096 * 32
+
+
+def test_backward_and_decode_work():
+    w = si.WORKLOADS[2]
+    assert bench.backward_flops(w) == 10.0 * 128 * 25167872 * 32
+    w4 = si.WORKLOADS[4]
+    assert bench.decode_step_bytes(w4) == 1075052544
+
+
+def _note(tmp_path, monkeypatch, family, workload, kind, body, sha):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    p = tmp_path / ("%s_%s_%s.md" % (family, workload, kind))
     p.write_text(body + "\nkernel_sources_sha256: %s\n" % sha)
-    return str(p)
 
 
-def test_note_parsers_follow_the_kernel_source_hash(tmp_path, monkeypatch):
-    sha = bench.kernel_sources_sha256()
-    monkeypatch.setattr(bench, "TRAFFIC_NOTE", _note(tmp_path, "traffic_bytes_per_launch: 123456", sha))
-    assert bench.recorded_traffic() == 123456
-    monkeypatch.setattr(bench, "MFMA_NOTE", _note(tmp_path, "mfma_busy_frac: 0.5", sha))
-    assert bench.recorded_mfma_busy() == 0.5
-    monkeypatch.setattr(bench, "SCLK_NOTE", _note(tmp_path, "sclk_ghz_timed: 2.0", sha))
-    assert bench.recorded_sclk() == 2.0
-    stale = "0" * 64
-    monkeypatch.setattr(bench, "TRAFFIC_NOTE", _note(tmp_path, "traffic_bytes_per_launch: 123456", stale))
-    monkeypatch.setattr(bench, "MFMA_NOTE", _note(tmp_path, "mfma_busy_frac: 0.5", stale))
-    monkeypatch.setattr(bench, "SCLK_NOTE", _note(tmp_path, "sclk_ghz_timed: 2.0", stale))
-    assert bench.recorded_traffic() is None and bench.recorded_mfma_busy() is None and bench.recorded_sclk() is None
-    monkeypatch.setattr(bench, "TRAFFIC_NOTE", str(tmp_path / "missing.md"))
-    assert bench.recorded_traffic() is None
+def test_note_parser_follows_the_kernel_source_hash(tmp_path, monkeypatch):
+    for fam in bench.KERNEL_SOURCES:
+        sha = bench.kernel_sources_sha256(fam)
+        _note(tmp_path, monkeypatch, fam, "wl", "traffic", "traffic_bytes_per_launch: 123456", sha)
+        assert bench.recorded(fam, "wl", "traffic", "traffic_bytes_per_launch") == 123456
+        _note(tmp_path, monkeypatch, fam, "wl", "mfma", "mfma_busy_frac: 0.5", "0" * 64)
+        assert bench.recorded(fam, "wl", "mfma", "mfma_busy_frac") is None
+        assert bench.recorded(fam, "other", "traffic", "traffic_bytes_per_launch") is None
+
+
+def test_committed_notes_parse():
+    """Every counter note under profiles/ names its kernel sources' hash and
+    carries the figure its kind promises."""
+    keys = {"traffic": "traffic_bytes_per_launch", "mfma": "mfma_busy_frac", "sclk": "sclk_ghz_timed"}
+    for f in os.listdir(bench.PROFILES):
+        m = __import__("re").match(r"(prefill_pp_kernel|decode_split_kernel|backward)_(.+)_(traffic|mfma|sclk)\.md$", f)
+        if not m:
+            continue
+        text = open(os.path.join(bench.PROFILES, f)).read()
+        assert "kernel_sources_sha256:" in text, f
+        assert keys[m.group(3)] + ":" in text, f
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -20,6 +20,8 @@ def run_chunked(q, k, v, s, r, chunk, rope_base, *, save_at=None):
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    if rope_base:
+        kd = swa.rope_keys(kd, 0, rope_base)    # every key rotated once, at its position
     kc, vc = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
     out = torch.empty_like(qd)
     for p0 in range(0, L, chunk):
@@ -78,7 +80,8 @@ def test_single_chunk_rope_equals_plain_rope_prefill(gpu):
     B, Hq, Hkv, L, d, s, r = 1, 2, 2, 500, 64, 4, 60
     q, k, v = seq_inputs(12, B, Hq, Hkv, L, d)
     say("single chunk rope d=64")
-    o = swa.prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), s, r, rope_base=10000.0)
+    o = swa.prefill(dev(q, "bf16"), swa.rope_keys(dev(k, "bf16"), 0, 10000.0), dev(v, "bf16"), s, r,
+                    rope_base=10000.0)
     ref = oracle.prefill_rows(q, k, v, s, r, rope_base=10000.0).reshape(o.shape)
     assert max_err(host(o), ref) <= TOL["bf16"]
 

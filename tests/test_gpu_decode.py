@@ -49,6 +49,27 @@ def test_append_bit_exact(gpu, s, r, pos0, n):
     assert_cache_equal(kc, vc, sim)
 
 
+@pytest.mark.parametrize("n,pos0,d,base", [
+    (300, 0, 128, 1e4), (70, 4090, 64, 500.0), (33, 131000, 128, 1e4), (5, (1 << 29) + 12345, 128, 1e4),
+])
+def test_rope_keys_matches_oracle(gpu, n, pos0, d, base):
+    """Keys rotated at their positions (pairs j, j + d/2, angle p * base^(-2j/d)):
+    every element against the oracle's fp64 rotation of the same bf16 row,
+    within one bf16 step; positions up to 2^29 (fp64 angles in turns)."""
+    import sliding_window_attention_sink_amd as swa
+    B, Hkv = 2, 3
+    g = np.random.default_rng(n + d + pos0 % 1000)
+    k = si.round_bf16(g.standard_normal((B, Hkv, n, d)).astype(np.float32))
+    say("rope keys", n, pos0, d, base)
+    got = host(swa.rope_keys(dev(k, "bf16"), pos0, base))
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(Hkv):
+            for i in range(n):
+                ref = oracle.rope(k[b, h, i], pos0 + i, base)
+                assert np.all(np.abs(got[b, h, i] - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-5), (b, h, i)
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,d,s,r,n_split", [
     (2, 8, 2, 128, 4, 60, 0),
     (2, 8, 2, 128, 4, 60, 3),
@@ -120,8 +141,8 @@ def test_decode_step_equals_append_then_decode(gpu, B, Hq, Hkv, d, s, r, n_split
     (1, 2, 1, 128, 70, 30, 1, 1e4),
 ])
 def test_decode_rope_matches_oracle(gpu, B, Hq, Hkv, d, s, r, n_split, base):
-    """RoPE re-positioning on the pre-rotation cache (the streaming
-    generation step): T = 1 .. 2(s+r)+20 through sink, filling and wrapped
+    """RoPE re-positioning (the streaming generation step; keys stored
+    rotated at their positions): T = 1 .. 2(s+r)+20 through sink, filling and wrapped
     slots, fused and unfused steps, against the fp64 row definition."""
     import sliding_window_attention_sink_amd as swa
     steps = 2 * (s + r) + 20
@@ -132,6 +153,7 @@ def test_decode_rope_matches_oracle(gpu, B, Hq, Hkv, d, s, r, n_split, base):
     kc1, vc1 = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
     kc2, vc2 = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
     Kd, Vd, Qd = dev(K, "bf16"), dev(V, "bf16"), dev(Q, "bf16")
+    Kd = swa.rope_keys(Kd, 0, base)      # keys enter rotated at their positions
     o1 = torch.empty((steps, B, Hq, d), dtype=torch.bfloat16, device="cuda")
     o2 = torch.empty_like(o1)
     say("decode rope", B, Hq, Hkv, d, s, r, n_split, base)
@@ -159,6 +181,7 @@ def test_decode_rope_equals_one_token_chunks(gpu):
     Q = si.round_bf16(g.standard_normal((B, Hq, steps, d)).astype(np.float32))
     kc, vc = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
     Kd, Vd, Qd = dev(K, "bf16"), dev(V, "bf16"), dev(Q, "bf16")
+    Kd = swa.rope_keys(Kd, 0, base)
     say("decode rope vs chunk 1")
     worst = 0.0
     for t in range(steps):
@@ -242,7 +265,7 @@ def test_decode_b64_gqa_full(gpu):
 def test_decode_rope_full_size_sampled(gpu):
     """The RoPE-re-positioning generation step at the bench's size (B=64,
     GQA 32/8, d=128, s=4, r=4092, 8192-token history): 8 fused steps on the
-    pre-rotation cache, every head of two sequences checked against the fp64
+    RoPE cache, every head of two sequences checked against the fp64
     row definition (keys of U(t) at cache positions 0..|U(t)|-1)."""
     import sliding_window_attention_sink_amd as swa
     w = si.WORKLOADS[4]
@@ -252,10 +275,12 @@ def test_decode_rope_full_size_sampled(gpu):
     say("decode rope full size: pre-fill", w.name)
     kc, vc = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda", fill=float("nan"))
     hkd, hvd = dev(hk, "bf16"), dev(hv, "bf16")
-    swa.cache_append(hkd, hvd, kc, vc, 0, w.s, w.r)
+    swa.cache_append(swa.rope_keys(hkd, 0, base), hvd, kc, vc, 0, w.s, w.r)
     torch.cuda.synchronize()
     del hkd, hvd
     qd, kd, vd = dev(qs, "bf16"), dev(ks, "bf16"), dev(vs, "bf16")
+    # step i's key rotated at its position L + i
+    kd = torch.stack([swa.rope_keys(kd[i].unsqueeze(2), w.L + i, base)[:, :, 0] for i in range(nsteps)])
     outs = torch.empty((nsteps, w.B, w.Hq, w.d), dtype=torch.bfloat16, device="cuda")
     say("decode rope full size: steps", w.name)
     for i in range(nsteps):

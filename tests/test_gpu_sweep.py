@@ -148,6 +148,8 @@ def test_sweep_matches_oracle(gpu, c):
         T = L + n_dec
         q, k, v = inputs(c, T)
         qd, kd, vd = dev(q, dt), dev(k, dt), dev(v, dt)
+        if base:
+            kd = swa.rope_keys(kd, 0, base)
         kc, vc = swa.new_cache(B, Hkv, d, s, r, torch.bfloat16, "cuda", fill=float("nan"))
         out = torch.empty((B, Hq, T, d), dtype=torch.bfloat16, device="cuda")
         p0 = 0
