@@ -314,7 +314,7 @@ def backward_flops(w) -> float:
     return 10.0 * w.d * key_count_sum(w.L, w.s, w.r) * w.B * w.Hq
 
 
-def bench_backward(torch, swa, w, steps=3, settle=_no_settle):
+def bench_backward(torch, swa, w, steps=5, settle=_no_settle):
     """Backward (dq, dk, dv) of a prefill workload's rows for a random upstream
     gradient, against the bf16 MFMA peak at 10 d flops per pair."""
     q, k, v = __import__("swa_inputs").prefill_inputs(w)
@@ -564,13 +564,16 @@ def main():
         log("w4", r4)
         torch.cuda.empty_cache()
     if 9 in todo:
-        rb = bench_backward(torch, swa, w2, settle=settle)
-        rooflines["backward_" + w2.name] = {
-            "bound": "mfma", "kernel": "swa_backward (bwd_q + bwd_kv kernels)", "achieved": rb["tflops"],
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": rb["tflops"] / PEAK_BF16_TFLOPS,
-            "flops_per_call": rb["flops"], "call_ms": rb["ms"]}
-        log("backward", rb)
-        torch.cuda.empty_cache()
+        # the backward on the GQA prefill's shape (no sinks) and on the 4+1020
+        # shape (sink keys seen by every later query)
+        for wb in (w2, si.WORKLOADS[3]):
+            rb = bench_backward(torch, swa, wb, settle=settle)
+            rooflines["backward_" + wb.name] = {
+                "bound": "mfma", "kernel": "swa_backward (bwd_dq + bwd_dkdv + bwd_reduce kernels)",
+                "achieved": rb["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": rb["tflops"] / PEAK_BF16_TFLOPS, "flops_per_call": rb["flops"], "call_ms": rb["ms"]}
+            log("backward", wb.name, rb)
+            torch.cuda.empty_cache()
     if 6 in todo:
         # window sweep on the GQA workload's tensors, to the full-attention limit
         extra["window_sweep_" + w2.name] = bench_window_sweep(torch, swa, w2, [512, 1024, 2048, 4096, 8192],

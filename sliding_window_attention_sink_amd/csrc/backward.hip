@@ -1,4 +1,5 @@
-// Backward of the windowed rows (training), bf16 inputs, fp32 gradients, gfx950.
+// Backward of the windowed rows (training) on the matrix units, bf16 inputs,
+// fp32 gradients, gfx950.
 //
 // The forward row t is softmax over U(t) = {i <= t : i < s or i >= t-r+1}
 // of scale * q_t . k_i, weighting v_i (hyper.ai summary of arXiv
@@ -10,21 +11,37 @@
 //   dQ_t = scale sum_{i in U(t)} dS_ti k_i,   dK_i = scale sum_t dS_ti q_t
 // with dK and dV summed over the q-heads of a kv-head.
 //
-// Three kernels on the vector units (a plain first backward, not
-// MFMA-tiled): dot products as bf16 pairs into fp32 (v_dot2c_f32_bf16, the
-// inputs exact), sums in fp32.  A wave takes eight adjacent rows or keys, so
-// each row a lane reads from memory serves eight dot products; the rows
-// staged for the dot products and each chunk's dS (and P) go through LDS:
-//   bwd_q:   per eight query rows, D_t, then one pass over the union of
-//            their keys (lanes score keys, then lanes over dims add
-//            dS_ti k_i) with the softmax normalised at the end, as in the
-//            forward's online softmax; lse and D go to the workspace.
-//   bwd_kv:  per eight keys, the queries t = i .. min(L-1, i+r-1) of each
-//            key i from every q-head of its group (for i >= s these are all
-//            of its queries): dK_i, dV_i, stored.
-//   bwd_sink: per sink key i < s and segment of the queries t >= i + r (the
-//            sinks are attended by every later query), the same sums, added
-//            atomically after bwd_kv's stores.
+// Two kernels, both tiled in 32x32 blocks on v_mfma_f32_32x32x16_bf16, with
+// the block operands staged in LDS by direct global->LDS loads (three
+// buffer sets, loads two blocks ahead):
+//
+//   bwd_dq (query-outer, like the forward): a wave owns 32 query rows with
+//     q and dO in registers and walks the key blocks of their key sets
+//     (the sink block, then the band; blocks outside are never loaded):
+//       S^T = K Q^T and dP^T = V dO^T (16 MFMAs), an online softmax over
+//       the keys (running max lazily raised, as in the forward), dS^T =
+//       P^T (dP^T - D) packed to bf16, dQ^T += K^T dS^T (8 MFMAs, K read
+//       transposed from LDS).  It also writes the row's log-sum-exp and
+//       D_t for the second kernel.
+//   bwd_dkdv (key-outer): a wave owns 32 keys with K and V in registers
+//     and walks the 32-row query blocks of every q-head of the kv-head
+//     that see them: S = Q K^T and dP = dO V^T (16 MFMAs), P from the
+//     row's log-sum-exp, dS = P (dP - D), then dV^T += dO^T P and dK^T +=
+//     Q^T dS (16 MFMAs, Q and dO read transposed from LDS).  A key tile
+//     (128 keys, four waves) whose queries span more than one segment is
+//     split into segments; segment 0 stores its sums, the others store
+//     partial sums that bwd_reduce adds in a fixed order (sink keys see
+//     every later query, so their tiles take many segments).  No atomics:
+//     the gradients are the same on every call.
+//
+// Rows of an MFMA block enter in the order swap23(m) (bits 2 and 3 of the
+// row index swapped), so that each lane's eight accumulator values of one
+// half are eight consecutive rows: the score accumulators are then the
+// bf16 B operands of the next products as they are.  Block tiles are
+// row-major with the 16-byte chunks of row r rotated by sw(r), which keeps
+// both the row reads (16 rows x one chunk) and the transposing reads
+// (ds_read_b64_tr_b16: 4 rows x 64 bytes per 32 lanes) free of LDS bank
+// conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,382 +50,525 @@
 namespace swa {
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int BW = 4;               // waves per workgroup
-constexpr int BT = 64 * BW;
+constexpr int NW = 4;              // waves per workgroup
+constexpr int NT = 64 * NW;
+constexpr int BLK = 32;            // rows of an MFMA block
+constexpr int NBUF = 3;            // LDS buffer sets
+constexpr float RESCALE_TH = 8.0f; // log2 units: raise the running max only past 2^8
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+// Block row held by accumulator element i of lane group g (rows fed in swap23 order).
+__device__ __forceinline__ constexpr int crow(int i, int g) { return 16 * (i / 8) + 8 * g + (i % 8); }
 
-// This lane's D / 64 consecutive dims of a bf16 row, as fp32.
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+    // max of lanes l and l^32 (v_permlane32_swap hands each lane both halves)
+    const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+    const auto sw = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+    return fmaxf(x, fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    // x of lane l plus x of lane l^32 (the swap hands each lane both)
+    const uint32_t xb = __builtin_bit_cast(uint32_t, x);
+    const auto sw = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+    return __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+}
+
+// Maps blockIdx to a work item so that each XCD (blocks are dealt to the 8
+// XCDs round-robin) gets one contiguous run of work items, whose operand
+// tiles then share that XCD's L2.
+__device__ __forceinline__ int xcd_item(int bid, int nblk) {
+    const int x = bid & 7, k = bid >> 3;
+    const int per = nblk >> 3, rem = nblk & 7;
+    return x * per + (x < rem ? x : rem) + k;
+}
+
+// One 16-byte direct global->LDS load per active lane: lane l's chunk lands
+// at lds + 16 l (lds is wave-uniform).  The kernels wait for these loads
+// themselves (wait_vm) before the barrier that publishes a block.
+__device__ __forceinline__ void load_lds16(const void* gp, void* lds) {
+    const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(la) : "m0");
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding.
+__device__ __forceinline__ void wait_vm(int n) {
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (n == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+}
+
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// A block tile: 32 rows of D bf16 values, row-major, the 16-byte chunk c of
+// row r stored at chunk c ^ sw(r).
 template <int D>
-__device__ __forceinline__ void lane_dims(const __bf16* row, int lane, float (&x)[D / 64]) {
-    if constexpr (D == 128) {
-        const uint32_t w = *(const uint32_t*)(row + 2 * lane);
-        x[0] = bf_lo(w);
-        x[1] = bf_hi(w);
-    } else {
-        x[0] = (float)row[lane];
+struct Tile {
+    static constexpr int CH = D / 8;         // chunks per row
+    static constexpr int KS = D / 16;        // k-steps over the head dim
+    static constexpr int NDB = D / 32;       // 32-dim blocks
+    static constexpr int RB = D * 2;         // bytes per row
+    static constexpr int BYTES = BLK * RB;
+    static constexpr int NINS = BYTES / 1024;  // direct-load instructions per tile
+    static constexpr int JW = NINS / NW;       // ... per wave
+    static_assert(JW >= 1 && NINS % NW == 0, "tile shape");
+
+    static __device__ __forceinline__ int sw(int r) {
+        return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
     }
-}
+    static __device__ __forceinline__ int off(int r, int c) { return r * RB + ((c ^ sw(r)) << 4); }
 
-__device__ __forceinline__ float wave_sum(float x) {
+    // Row operand of k-step ks for MFMA row l32 (tile row swap23(l32), dims
+    // 16 ks + 8 g .. +7): the A operand of a product over the head dim.
+    static __device__ __forceinline__ bf16x8 rowop(const char* t, int l32, int g, int ks) {
+        return *(const bf16x8*)(t + off(swap23(l32), 2 * ks + g));
+    }
+
+    // Transposed operand [dim x row] of d-block db, k-step kk: lane (l32, g)
+    // gets dim 32 db + l32 of tile rows 16 kk + 8 g .. +7.  ds_read_b64_tr_b16
+    // hands lane 16q + 4a + j element e of the four values lane 16q + a + 4e
+    // reads; that lane reads row 16 kk + 8 (q / 2) + e (+4 for the second
+    // read), dims 32 db + 16 (q & 1) + 4a .. +3.
+    static __device__ __forceinline__ bf16x8 trop(const char* t, int lane, int db, int kk) {
+        const int a = lane & 3, e = (lane >> 2) & 3, q = lane >> 4;
+        const int row = 16 * kk + 8 * (q >> 1) + e;
+        const int c = 4 * db + 2 * (q & 1) + (a >> 1);
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + off(row, c) + 8 * (a & 1)));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + off(row + 4, c) + 8 * (a & 1)));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+
+    // This wave's share of the direct loads of a tile whose row x is global
+    // row base + clamp(row0 + x) (clamped into [lo, hi]; a clamped row is
+    // real data the masks then drop).
+    static __device__ __forceinline__ void load(char* t, const __bf16* base, int row0, int lo, int hi, int wave,
+                                                int lane) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
+        for (int j = 0; j < JW; ++j) {
+            const int ins = wave + NW * j;
+            const int x = 64 * ins + lane;
+            const int r = x / CH, phys = x % CH;
+            int gr = row0 + r;
+            gr = gr < lo ? lo : (gr > hi ? hi : gr);
+            load_lds16(base + (size_t)gr * D + 8 * (phys ^ sw(r)), t + 1024 * ins);
+        }
+    }
+};
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
+// U(t) membership of key i for query t (bitwise, so it compiles to selects,
+// not branches).
+__device__ __forceinline__ bool in_set(int t, int i, int s, int r) { return (i <= t) & ((i < s) | (i >= t - r + 1)); }
 
-// LDS rows written by the wave's lanes are read by all of them next; LDS
-// accesses of one wave complete in order, the clobber keeps the compiler's.
-__device__ __forceinline__ void lds_order() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Stage two bf16 rows of D values into LDS as they are (bf16 pairs, lanes
-// over pairs).
+// ---------------------------------------------------------------------------
+// dQ, per-row log-sum-exp and D.
 template <int D>
-__device__ __forceinline__ void stage2(uint32_t* xa, uint32_t* xb, const __bf16* ra, const __bf16* rb, int lane) {
-    for (int e = lane; e < D / 2; e += 64) {
-        xa[e] = ((const uint32_t*)ra)[e];
-        xb[e] = ((const uint32_t*)rb)[e];
-    }
-}
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BackwardArgs a) {
+    typedef Tile<D> TT;
+    constexpr int KS = TT::KS, NDB = TT::NDB;
+    __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TT::BYTES];
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// a[0] b[0] + a[1] b[1] + acc for two bf16 pairs (products exact in fp32)
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
-}
-
-// R dot products at once: x holds R bf16 rows of D values (LDS, as pairs,
-// row stride D / 2 words), row is one bf16 row (global memory), read once
-// for all R.  Pairs 0-1 of every 4 go to one accumulator chain and 2-3 to
-// another, so the result does not depend on which operand sits in LDS.
-template <int D, int R>
-__device__ __forceinline__ void dot_rows(const uint32_t* x, const __bf16* row, float (&out)[R]) {
-    float c0[R], c1[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) c0[q] = c1[q] = 0.0f;
-#pragma unroll 4
-    for (int c = 0; c < D / 8; ++c) {
-        const u32x4 w = *(const u32x4*)(row + 8 * c);
-#pragma unroll
-        for (int q = 0; q < R; ++q) {
-            const u32x4 a = *(const u32x4*)(x + q * (D / 2) + 4 * c);
-            c0[q] = dot2(a[0], w[0], c0[q]);
-            c0[q] = dot2(a[1], w[1], c0[q]);
-            c1[q] = dot2(a[2], w[2], c1[q]);
-            c1[q] = dot2(a[3], w[3], c1[q]);
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < R; ++q) out[q] = c0[q] + c1[q];
-}
-
-// Rows (or keys) per wave in bwd_q and bwd_kv: every K, V, Q or dout row a
-// lane reads serves RW of them (8 ran 11% faster than 4 on the main
-// workload's shape, at 141-179 VGPRs).
-constexpr int RW = 8;
-
-template <int D>
-__global__ __launch_bounds__(BT) void bwd_q_kernel(BackwardArgs a) {
-    constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) uint32_t xs[BW][2][RW * D / 2];
-    __shared__ __attribute__((aligned(16))) float bc[BW][64 * RW];   // a chunk's dS, [pair][row]
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t ngr = (a.L + RW - 1) / RW;                 // row groups per (b, h)
-    const int64_t grp = (int64_t)blockIdx.x * BW + wv;       // (b * Hq + h) * ngr + row group
-    if (grp >= (int64_t)a.B * a.Hq * ngr) return;
-    const int64_t bh = grp / ngr;
-    const int tb = (int)(grp % ngr) * RW;                    // rows tb .. tl
-    const int nr = a.L - tb < RW ? (int)(a.L - tb) : RW;
-    const int tl = tb + nr - 1;
-    const int b = (int)(bh / a.Hq), h = (int)(bh % a.Hq);
-    const int kvh = h / (a.Hq / a.Hkv);
-    const __bf16* kb = (const __bf16*)a.k + ((int64_t)b * a.Hkv + kvh) * a.L * D;
-    const __bf16* vb = (const __bf16*)a.v + ((int64_t)b * a.Hkv + kvh) * a.L * D;
-    const int64_t row0 = bh * a.L + tb;
-    uint32_t* qs = xs[wv][0];
-    uint32_t* gs = xs[wv][1];
-    // rows past the end stage row tl again (their results are not stored)
-#pragma unroll
-    for (int x = 0; x < RW; ++x) {
-        const int64_t rx = row0 + (x < nr ? x : nr - 1);
-        stage2<D>(qs + x * (D / 2), gs + x * (D / 2), (const __bf16*)a.q + rx * D, (const __bf16*)a.dout + rx * D,
-                  lane);
-    }
-    lds_order();
-    float Dt[RW];
-#pragma unroll
-    for (int x = 0; x < RW; ++x) {
-        const uint32_t* orow = (const uint32_t*)((const __bf16*)a.o + (row0 + (x < nr ? x : nr - 1)) * D);
-        float dpart = 0.0f;
-        for (int e = lane; e < D / 2; e += 64) {
-            const uint32_t gw = gs[x * (D / 2) + e], ow = orow[e];
-            dpart += bf_lo(gw) * bf_lo(ow) + bf_hi(gw) * bf_hi(ow);
-        }
-        Dt[x] = wave_sum(dpart);
-    }
-
-    // keys of any of the rows: sinks 0 .. ns-1, then the window wlo .. tl;
-    // key i is in U(tb + x) iff i <= tb + x and (i < s or i >= tb + x - r + 1)
-    const int ns = a.s < tl + 1 ? a.s : tl + 1;
-    const int wlo = a.s > tb - a.r + 1 ? a.s : tb - a.r + 1;
-    const int n = ns + (tl >= wlo ? tl - wlo + 1 : 0);
-    auto key_of = [&](int j) { return j < ns ? j : wlo + (j - ns); };
-    auto in_set = [&](int x, int i) { return x < nr && i <= tb + x && (i < a.s || i >= tb + x - a.r + 1); };
-    const float c = a.scale_log2e;
-
-    // one pass over the keys, the softmax normalised at the end: per row a
-    // running max m (the same in every lane), per lane a partial sum of
-    // exp2(score - m), and dQ accumulated against that m, all rescaled when m
-    // rises (dS_ti l_t = exp2(score - m) (dp - D_t) with l_t the row's sum)
-    float m[RW], lp[RW], acc[RW][NE];
-#pragma unroll
-    for (int x = 0; x < RW; ++x) {
-        m[x] = -__builtin_inff();
-        lp[x] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[x][e] = 0.0f;
-    }
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        const int j = j0 + lane;
-        float v[RW], dp[RW];
-#pragma unroll
-        for (int x = 0; x < RW; ++x) {
-            v[x] = -__builtin_inff();
-            dp[x] = 0.0f;
-        }
-        if (j < n) {
-            const int i = key_of(j);
-            float sc[RW];
-            dot_rows<D, RW>(qs, kb + (int64_t)i * D, sc);
-            dot_rows<D, RW>(gs, vb + (int64_t)i * D, dp);
-#pragma unroll
-            for (int x = 0; x < RW; ++x)
-                if (in_set(x, i)) v[x] = sc[x] * c;
-        }
-        float ds[RW];
-#pragma unroll
-        for (int x = 0; x < RW; ++x) {
-            const float mn = fmaxf(m[x], wave_max(v[x]));
-            if (mn > m[x]) {
-                const float alpha = exp2f(m[x] - mn);     // 0 while m is -inf
-                lp[x] *= alpha;
-#pragma unroll
-                for (int e = 0; e < NE; ++e) acc[x][e] *= alpha;
-                m[x] = mn;
-            }
-            const float p = v[x] == -__builtin_inff() ? 0.0f : exp2f(v[x] - m[x]);
-            lp[x] += p;
-            ds[x] = p * (dp[x] - Dt[x]);
-        }
-        // the chunk's (unnormalised) dS through LDS: each key's RW values
-        // come back as broadcast reads in the dims loop
-#pragma unroll
-        for (int x = 0; x < RW; ++x) bc[wv][lane * RW + x] = ds[x];
-        lds_order();
-        const int cnt = n - j0 < 64 ? n - j0 : 64;
-#pragma unroll 2
-        for (int jj = 0; jj < cnt; ++jj) {
-            float kx[NE];
-            lane_dims<D>(kb + (int64_t)key_of(j0 + jj) * D, lane, kx);
-            const float* g = &bc[wv][jj * RW];
-#pragma unroll
-            for (int x = 0; x < RW; ++x) {
-#pragma unroll
-                for (int e = 0; e < NE; ++e) acc[x][e] = fmaf(g[x], kx[e], acc[x][e]);
-            }
-        }
-        lds_order();
-    }
-#pragma unroll
-    for (int x = 0; x < RW; ++x) {
-        if (x >= nr) break;
-        const float l = wave_sum(lp[x]);
-        float* dq = a.dq + (row0 + x) * D + NE * lane;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) dq[e] = acc[x][e] * (a.scale / l);
-        if (lane == 0) {
-            a.lse2[row0 + x] = m[x] + log2f(l);
-            a.dd[row0 + x] = Dt[x];
-        }
-    }
-}
-
-// dK, dV contributions of R keys of kv-head kvh of batch b (K and V rows
-// staged in ks, vs, row stride D) from the queries t0 .. t0+nt-1 of every
-// q-head of the group, for the (key x, query t) pairs with ok(x, t); added
-// into dka, dva (this lane's dims).
-template <int D, int R, class Ok>
-__device__ __forceinline__ void kv_sums(const BackwardArgs& a, const uint32_t* ks, const uint32_t* vs, float* bc,
-                                        int b, int kvh, int t0, int nt, int lane, Ok&& ok, float (&dka)[R][D / 64],
-                                        float (&dva)[R][D / 64]) {
-    constexpr int NE = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+    const int L = (int)a.L, s = a.s, r = a.r;
     const int G = a.Hq / a.Hkv;
-    const int n = nt * G;
+    const int nqt = (L + 127) / 128;
+    // late (heavier) query tiles first; the q-heads of a kv-head adjacent
+    const int bid = xcd_item(blockIdx.x, gridDim.x);
+    const int qt = nqt - 1 - (bid / a.Hq) % nqt;
+    const int bhq = (bid / (a.Hq * nqt)) * a.Hq + bid % a.Hq;   // b * Hq + h
+    const int b = bhq / a.Hq, h = bhq % a.Hq, kvh = h / G;
+    const int t0 = qt * 128, t1 = (t0 + 127) < (L - 1) ? (t0 + 127) : (L - 1);
+    const int tw0 = t0 + 32 * wave, tw1 = (tw0 + 31) < t1 ? (tw0 + 31) : t1;
+    const bool wave_active = tw0 <= t1;
+    const int my_t = tw0 + l32;
+    const bool my_valid = my_t <= t1;
+    const size_t rowq = (size_t)bhq * L + (my_valid ? my_t : t1);
+
+    const __bf16* kg = (const __bf16*)a.k + (size_t)(b * a.Hkv + kvh) * L * D;
+    const __bf16* vg = (const __bf16*)a.v + (size_t)(b * a.Hkv + kvh) * L * D;
+
+    // q and dO as B operands (lane: its row, dims 16 ks + 8 g .. +7); D_t
+    bf16x8 qB[KS], dB[KS];
+    float Dt;
+    {
+        const __bf16* qr = (const __bf16*)a.q + rowq * D;
+        const __bf16* dr = (const __bf16*)a.dout + rowq * D;
+        const __bf16* orow = (const __bf16*)a.o + rowq * D;
+        float part = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qB[ks] = *(const bf16x8*)(qr + 16 * ks + 8 * g);
+            dB[ks] = *(const bf16x8*)(dr + 16 * ks + 8 * g);
+            const bf16x8 ov = *(const bf16x8*)(orow + 16 * ks + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += (float)dB[ks][e] * (float)ov[e];
+        }
+        Dt = pair_sum(part);
+    }
+
+    // key blocks: the sink block(s) [0, min(s, t1+1)) and the band
+    // [max(s, t0-r+1), t1], as one list (merged when they touch)
+    const int sink_end = s < t1 + 1 ? s : t1 + 1;
+    const int band_lo = s > t0 - r + 1 ? s : t0 - r + 1;
+    int n0 = sink_end > 0 ? (sink_end - 1) / BLK + 1 : 0;
+    int bf = band_lo <= t1 ? band_lo / BLK : 0;
+    int n1 = band_lo <= t1 ? t1 / BLK - bf + 1 : 0;
+    if (n0 > 0 && n1 > 0 && bf <= n0) {   // contiguous: one run [0, t1 / BLK]
+        n1 = t1 / BLK - n0 + 1;
+        bf = n0;
+    }
+    const int nv = n0 + n1;
+    auto blk_of = [&](int v) __attribute__((always_inline)) { return v < n0 ? v : bf + (v - n0); };
+
+    auto issue = [&](int v, int buf) __attribute__((always_inline)) {
+        const int kb = blk_of(v) * BLK;
+        TT::load(smem[buf][0], kg, kb, 0, L - 1, wave, lane);
+        TT::load(smem[buf][1], vg, kb, 0, L - 1, wave, lane);
+    };
+
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    float m_c = -__builtin_inff(), l_part = 0.0f;
     const float c = a.scale_log2e;
-    auto qrow_of = [&](int j) { return ((int64_t)b * a.Hq + kvh * G + j % G) * a.L + t0 + j / G; };
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        const int j = j0 + lane;
-        float p[R], ds[R];
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q, dO, o are in registers
+    if (nv > 0) issue(0, 0);
+    if (nv > 1) issue(1, 1);
+    int buf = 0;
+    for (int v = 0; v < nv; ++v) {
+        wait_vm(v + 1 < nv ? 2 * TT::JW : 0);
+        wg_barrier();
+        if (v + 2 < nv) issue(v + 2, buf == 0 ? 2 : buf - 1);
+        const int kb = blk_of(v) * BLK;
+        const bool need = wave_active && kb <= tw1 && (kb < s || kb + BLK - 1 >= tw0 - r + 1);
+        if (need) {
+            const char* Kt = smem[buf][0];
+            const char* Vt = smem[buf][1];
+            f32x16 sa = {}, pa = {};
 #pragma unroll
-        for (int x = 0; x < R; ++x) p[x] = ds[x] = 0.0f;
-        if (j < n) {
-            const int64_t qr = qrow_of(j);
-            const int t = t0 + j / G;
-            float sc[R], dp[R];
-            dot_rows<D, R>(ks, (const __bf16*)a.q + qr * D, sc);
-            dot_rows<D, R>(vs, (const __bf16*)a.dout + qr * D, dp);
-            const float l2 = a.lse2[qr], dd = a.dd[qr];
-#pragma unroll
-            for (int x = 0; x < R; ++x) {
-                if (!ok(x, t)) continue;
-                p[x] = exp2f(sc[x] * c - l2);
-                ds[x] = p[x] * (dp[x] - dd);
+            for (int ks = 0; ks < KS; ++ks) {
+                sa = mfma(TT::rowop(Kt, l32, g, ks), qB[ks], sa);
+                pa = mfma(TT::rowop(Vt, l32, g, ks), dB[ks], pa);
             }
+            const bool full = kb + BLK - 1 <= tw0 && (kb + BLK - 1 < s || kb >= tw1 - r + 1);
+            if (!full) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    sa[i] = (my_valid & in_set(my_t, kb + crow(i, g), s, r)) ? sa[i] : -__builtin_inff();
+            }
+            float mx = sa[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sa[i]);
+            mx = pair_max(mx);
+            const float mxc = mx * c;
+            const bool upd = mxc > m_c + RESCALE_TH;
+            if (__builtin_amdgcn_ballot_w64(upd)) {
+                const float alpha = upd ? __builtin_amdgcn_exp2f(m_c - mxc) : 1.0f;
+                m_c = upd ? mxc : m_c;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+            }
+            const float mneg = m_c == -__builtin_inff() ? 0.0f : -m_c;
+            bf16x8 ds[2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, mneg));
+                l_part += p;
+                ds[i / 8][i % 8] = (__bf16)(p * (pa[i] - Dt));
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) acc[db] = mfma(TT::trop(Kt, lane, db, kk), ds[kk], acc[db]);
         }
-        // the chunk's P and dS through LDS ([pair][P of the R keys, dS of
-        // the R keys]), read back as broadcasts in the dims loop
+        buf = buf == 2 ? 0 : buf + 1;
+    }
+    if (!my_valid) return;
+    const float l_tot = pair_sum(l_part);
+    const float inv = a.scale / l_tot;
+    float* dq = a.dq + ((size_t)bhq * L + my_t) * D;
 #pragma unroll
-        for (int x = 0; x < R; ++x) {
-            bc[lane * 2 * R + x] = p[x];
-            bc[lane * 2 * R + R + x] = ds[x];
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = acc[db][4 * q4 + j] * inv;
+            *(f32x4*)(dq + 32 * db + 8 * q4 + 4 * g) = x;
         }
-        lds_order();
-        const int cnt = n - j0 < 64 ? n - j0 : 64;
-#pragma unroll 2
-        for (int jj = 0; jj < cnt; ++jj) {
-            const int64_t qr = qrow_of(j0 + jj);
-            float gx[NE], qx[NE];
-            lane_dims<D>((const __bf16*)a.dout + qr * D, lane, gx);
-            lane_dims<D>((const __bf16*)a.q + qr * D, lane, qx);
-            const float* pj = bc + jj * 2 * R;
+    if (g == 0) {
+        a.lse2[(size_t)bhq * L + my_t] = m_c + __builtin_amdgcn_logf(l_tot);
+        a.dd[(size_t)bhq * L + my_t] = Dt;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV.  Work items: (b * Hkv + kvh, key tile of 128 keys, segment);
+// first the tiles holding sink keys (their queries run to the end), then
+// the others.  Segment seg of a tile walks its query blocks
+// [qb_lo + seg * segb, ...) for every q-head of the kv-head.
+template <int D>
+__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid gr) {
+    typedef Tile<D> TT;
+    constexpr int KS = TT::KS, NDB = TT::NDB;
+    __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TT::BYTES];
+    __shared__ __attribute__((aligned(16))) float stat[NBUF][2][BLK];   // lse (log2 units), D
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+    const int L = (int)a.L, s = a.s, r = a.r;
+    const int G = a.Hq / a.Hkv;
+
+    // ---- work item
+    int bhk, tile, seg, nseg_max;
+    size_t slot_base;
+    {
+        // sink items (long) first and in their own order, which the
+        // round-robin dispatch spreads over the XCDs; the band items in XCD
+        // runs, so the key tiles that share query blocks share an L2
+        const int n_sink_items = gr.bhkv * gr.tiles_sink * gr.nseg_sink;
+        int id = (int)blockIdx.x < n_sink_items
+                     ? (int)blockIdx.x
+                     : n_sink_items + xcd_item((int)blockIdx.x - n_sink_items, (int)gridDim.x - n_sink_items);
+        if (id < n_sink_items) {
+            seg = id % gr.nseg_sink;
+            tile = (id / gr.nseg_sink) % gr.tiles_sink;
+            bhk = id / (gr.nseg_sink * gr.tiles_sink);
+            nseg_max = gr.nseg_sink;
+            slot_base = gr.slots_band + ((size_t)bhk * gr.tiles_sink + tile) * (gr.nseg_sink - 1);
+        } else {
+            id -= n_sink_items;
+            const int tb = gr.tiles - gr.tiles_sink;
+            seg = id % gr.nseg_band;
+            tile = gr.tiles_sink + (id / gr.nseg_band) % tb;
+            bhk = id / (gr.nseg_band * tb);
+            nseg_max = gr.nseg_band;
+            slot_base = ((size_t)bhk * tb + (tile - gr.tiles_sink)) * (gr.nseg_band - 1);
+        }
+    }
+    (void)nseg_max;
+    const int b = bhk / a.Hkv, kvh = bhk % a.Hkv;
+    const int i0 = tile * 128, i1 = (i0 + 127) < (L - 1) ? (i0 + 127) : (L - 1);
+    // query blocks of the tile: keys i0..i1 are seen by queries i0 .. i1 + r - 1
+    // (sink keys: every later query)
+    const int q_hi = i0 < s ? L - 1 : ((i1 + r - 1) < (L - 1) ? (i1 + r - 1) : (L - 1));
+    const int qb_lo = i0 / BLK, qb_hi = q_hi / BLK;
+    const int nb = qb_hi - qb_lo + 1;
+    const int sb0 = seg * gr.segb;
+    if (sb0 >= nb) return;                                 // an empty segment (all waves leave)
+    const int sb1 = (sb0 + gr.segb) < nb ? (sb0 + gr.segb) : nb;
+    const int niter = (sb1 - sb0) * G;
+
+    const int kw0 = i0 + 32 * wave;                        // this wave's keys kw0 .. kw0 + 31
+    const int my_key = kw0 + l32;
+    const bool wave_active = kw0 <= i1;
+    const __bf16* kg = (const __bf16*)a.k + (size_t)bhk * L * D;
+    const __bf16* vg = (const __bf16*)a.v + (size_t)bhk * L * D;
+
+    // K^T and V^T B operands of S = Q K^T and dP = dO V^T (lane: its key, dims 16 ks + 8 g .. +7)
+    bf16x8 kB[KS], vB[KS];
+    {
+        const int kr = my_key < L ? my_key : L - 1;
 #pragma unroll
-            for (int x = 0; x < R; ++x) {
+        for (int ks = 0; ks < KS; ++ks) {
+            kB[ks] = *(const bf16x8*)(kg + (size_t)kr * D + 16 * ks + 8 * g);
+            vB[ks] = *(const bf16x8*)(vg + (size_t)kr * D + 16 * ks + 8 * g);
+        }
+    }
+
+    // iteration it: query block qb = qb_lo + sb0 + it / G of q-head kvh * G + it % G
+    auto issue = [&](int it, int buf) __attribute__((always_inline)) {
+        const int qb = qb_lo + sb0 + it / G;
+        const int bhq = b * a.Hq + kvh * G + it % G;
+        const __bf16* qg = (const __bf16*)a.q + (size_t)bhq * L * D;
+        const __bf16* dg = (const __bf16*)a.dout + (size_t)bhq * L * D;
+        TT::load(smem[buf][0], qg, qb * BLK, 0, L - 1, wave, lane);
+        TT::load(smem[buf][1], dg, qb * BLK, 0, L - 1, wave, lane);
+        // lse and D of the block's 32 rows: 4 lanes of every wave, 16 bytes
+        // each (rows past L read the next head's values or the arrays'
+        // padding; the masks drop them)
+        if (lane < 4) {
+            const int x = 4 * wave + lane;                      // 16-byte piece 0..15
+            const float* src = (x < 8 ? a.lse2 : a.dd) + (size_t)bhq * L;
+            load_lds16(src + qb * BLK + 4 * (x & 7), &stat[buf][0][0] + 16 * wave);
+        }
+    };
+    // loads per wave per iteration: two tiles, one stat piece
+    constexpr int NLD = 2 * TT::JW + 1;
+
+    f32x16 dvT[NDB], dkT[NDB];
 #pragma unroll
-                for (int e = 0; e < NE; ++e) {
-                    dva[x][e] = fmaf(pj[x], gx[e], dva[x][e]);
-                    dka[x][e] = fmaf(pj[R + x], qx[e], dka[x][e]);
+    for (int db = 0; db < NDB; ++db) {
+        dvT[db] = f32x16{};
+        dkT[db] = f32x16{};
+    }
+    const float c = a.scale_log2e;
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K and V are in registers
+    issue(0, 0);
+    if (niter > 1) issue(1, 1);
+    int buf = 0;
+    for (int it = 0; it < niter; ++it) {
+        wait_vm(it + 1 < niter ? NLD : 0);
+        wg_barrier();
+        if (it + 2 < niter) issue(it + 2, buf == 0 ? 2 : buf - 1);
+        const int tq0 = (qb_lo + sb0 + it / G) * BLK;        // the block's queries tq0 .. tq0 + 31
+        const bool need = wave_active && kw0 <= tq0 + BLK - 1 && tq0 <= L - 1 &&
+                          (kw0 < s || kw0 + BLK - 1 >= tq0 - r + 1);
+        if (need) {
+            const char* Qt = smem[buf][0];
+            const char* Ot = smem[buf][1];   // dO
+            f32x16 sa = {}, pa = {};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sa = mfma(TT::rowop(Qt, l32, g, ks), kB[ks], sa);
+                pa = mfma(TT::rowop(Ot, l32, g, ks), vB[ks], pa);
+            }
+            // lse and D of this lane's 16 queries (rows 8g .. 8g+7, 16+8g .. +7)
+            const f32x4* ls = (const f32x4*)&stat[buf][0][0];
+            const f32x4* dd = (const f32x4*)&stat[buf][1][0];
+            f32x4 lq[4], dq4[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    lq[2 * h + u] = ls[(16 * h + 8 * g) / 4 + u];
+                    dq4[2 * h + u] = dd[(16 * h + 8 * g) / 4 + u];
+                }
+            const bool full = kw0 + BLK - 1 <= tq0 && tq0 + BLK - 1 <= L - 1 && kw0 + BLK - 1 <= L - 1 &&
+                              (kw0 + BLK - 1 < s || kw0 >= tq0 + BLK - 1 - r + 1);
+            bf16x8 pp[2], ps[2];
+            if (full) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq[i / 4][i % 4]));
+                    pp[i / 8][i % 8] = (__bf16)p;
+                    ps[i / 8][i % 8] = (__bf16)(p * (pa[i] - dq4[i / 4][i % 4]));
+                }
+            } else {
+                // masked pairs (and rows past L, whose statistics are not
+                // this head's) give P = dS = 0
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = tq0 + crow(i, g);
+                    const bool ok = (t <= L - 1) & (my_key <= L - 1) & in_set(t, my_key, s, r);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq[i / 4][i % 4]));
+                    const float dsv = p * (pa[i] - dq4[i / 4][i % 4]);
+                    pp[i / 8][i % 8] = (__bf16)(ok ? p : 0.0f);
+                    ps[i / 8][i % 8] = (__bf16)(ok ? dsv : 0.0f);
                 }
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dvT[db] = mfma(TT::trop(Ot, lane, db, kk), pp[kk], dvT[db]);
+                    dkT[db] = mfma(TT::trop(Qt, lane, db, kk), ps[kk], dkT[db]);
+                }
         }
-        lds_order();
+        buf = buf == 2 ? 0 : buf + 1;
     }
-}
-
-template <int D>
-__global__ __launch_bounds__(BT) void bwd_kv_kernel(BackwardArgs a) {
-    constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) uint32_t xs[BW][2][RW * D / 2];
-    __shared__ __attribute__((aligned(16))) float bc[BW][64 * 2 * RW];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t ngr = (a.L + RW - 1) / RW;                 // key groups per (b, kv-head)
-    const int64_t grp = (int64_t)blockIdx.x * BW + wv;       // (b * Hkv + kvh) * ngr + key group
-    if (grp >= (int64_t)a.B * a.Hkv * ngr) return;
-    const int64_t bk = grp / ngr;
-    const int ib = (int)(grp % ngr) * RW;                    // keys ib .. ib + nk - 1
-    const int nk = a.L - ib < RW ? (int)(a.L - ib) : RW;
-    const int b = (int)(bk / a.Hkv), kvh = (int)(bk % a.Hkv);
-    const int64_t key0 = bk * a.L + ib;
-    uint32_t* ks = xs[wv][0];
-    uint32_t* vs = xs[wv][1];
-#pragma unroll
-    for (int x = 0; x < RW; ++x) {
-        const int64_t kx = key0 + (x < nk ? x : nk - 1);
-        stage2<D>(ks + x * (D / 2), vs + x * (D / 2), (const __bf16*)a.k + kx * D, (const __bf16*)a.v + kx * D,
-                  lane);
+    if (!wave_active || my_key > L - 1) return;
+    // segment 0 stores the sums, the others partial sums for bwd_reduce
+    float *dk, *dv;
+    if (seg == 0) {
+        dk = a.dk + ((size_t)bhk * L + my_key) * D;
+        dv = a.dv + ((size_t)bhk * L + my_key) * D;
+    } else {
+        float* slot = a.part + (slot_base + seg - 1) * (size_t)(2 * 128 * D);
+        dk = slot + (size_t)(my_key - i0) * D;
+        dv = slot + (size_t)(128 + my_key - i0) * D;
     }
-    lds_order();
-    // key ib + x takes the queries ib + x .. ib + x + r - 1 (all of them for
-    // a key >= s; the first r for a sink, whose later ones bwd_sink adds)
-    const int64_t last = (int64_t)ib + nk - 1 + a.r - 1;
-    const int tend = (int)(last < a.L - 1 ? last : a.L - 1);
-    auto ok = [&](int x, int t) { return x < nk && t >= ib + x && (int64_t)t <= (int64_t)ib + x + a.r - 1; };
-    float dka[RW][NE], dva[RW][NE];
 #pragma unroll
-    for (int x = 0; x < RW; ++x)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < NE; ++e) dka[x][e] = dva[x][e] = 0.0f;
-    kv_sums<D, RW>(a, ks, vs, bc[wv], b, kvh, ib, tend - ib + 1, lane, ok, dka, dva);
+        for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 xk, xv;
 #pragma unroll
-    for (int x = 0; x < RW; ++x) {
-        if (x >= nk) break;
-        float* dk = a.dk + (key0 + x) * D + NE * lane;
-        float* dv = a.dv + (key0 + x) * D + NE * lane;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            dk[e] = dka[x][e] * a.scale;
-            dv[e] = dva[x][e];
+            for (int j = 0; j < 4; ++j) {
+                xk[j] = dkT[db][4 * q4 + j] * a.scale;
+                xv[j] = dvT[db][4 * q4 + j];
+            }
+            *(f32x4*)(dk + 32 * db + 8 * q4 + 4 * g) = xk;
+            *(f32x4*)(dv + 32 * db + 8 * q4 + 4 * g) = xv;
         }
-    }
 }
 
-// Sink key i < s, queries i + r + seg * kSinkSeg onwards (at most kSinkSeg
-// positions): added to bwd_kv's stored sums.
+// Adds the partial sums of segments 1 .. of every split key tile to dK and
+// dV, in segment order.  Thread: 4 values of one key.
 template <int D>
-__global__ __launch_bounds__(BT) void bwd_sink_kernel(BackwardArgs a, int32_t nseg) {
-    constexpr int NE = D / 64;
-    __shared__ __attribute__((aligned(16))) uint32_t xs[BW][2][D / 2];
-    __shared__ __attribute__((aligned(16))) float bc[BW][64 * 2];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t nitems = (int64_t)a.B * a.Hkv * a.s * nseg;
-    const int64_t item = (int64_t)blockIdx.x * BW + wv;    // ((b * Hkv + kvh) * s + i) * nseg + seg
-    if (item >= nitems) return;
-    const int seg = (int)(item % nseg);
-    const int64_t rest = item / nseg;
-    const int i = (int)(rest % a.s);
-    const int64_t bk = rest / a.s;
-    const int b = (int)(bk / a.Hkv), kvh = (int)(bk % a.Hkv);
-    const int64_t t0 = (int64_t)i + a.r + (int64_t)seg * kSinkSeg;
-    if (t0 > a.L - 1) return;
-    const int64_t t1 = t0 + kSinkSeg - 1 < a.L - 1 ? t0 + kSinkSeg - 1 : a.L - 1;
-    const int64_t key = bk * a.L + i;
-    uint32_t* ks = xs[wv][0];
-    uint32_t* vs = xs[wv][1];
-    stage2<D>(ks, vs, (const __bf16*)a.k + key * D, (const __bf16*)a.v + key * D, lane);
-    lds_order();
-    float dka[1][NE], dva[1][NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) dka[0][e] = dva[0][e] = 0.0f;
-    kv_sums<D, 1>(a, ks, vs, bc[wv], b, kvh, (int)t0, (int)(t1 - t0 + 1), lane, [](int, int) { return true; }, dka,
-                  dva);
-    float* dk = a.dk + key * D + NE * lane;
-    float* dv = a.dv + key * D + NE * lane;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-        atomicAdd(dk + e, dka[0][e] * a.scale);
-        atomicAdd(dv + e, dva[0][e]);
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardArgs a, BwdGrid gr) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_bh = a.L * (D / 4);
+    if (idx >= (int64_t)gr.bhkv * per_bh) return;
+    const int bhk = (int)(idx / per_bh);
+    const int key = (int)((idx % per_bh) / (D / 4));
+    const int e4 = (int)(idx % (D / 4)) * 4;
+    const int L = (int)a.L;
+    const int tile = key / 128, i0 = tile * 128;
+    const int i1 = (i0 + 127) < (L - 1) ? (i0 + 127) : (L - 1);
+    const bool sink = tile < gr.tiles_sink;
+    const int q_hi = sink ? L - 1 : ((i1 + a.r - 1) < (L - 1) ? (i1 + a.r - 1) : (L - 1));
+    const int nb = q_hi / BLK - i0 / BLK + 1;
+    const int nseg = (nb + gr.segb - 1) / gr.segb;
+    if (nseg <= 1) return;
+    const size_t base = sink ? gr.slots_band + ((size_t)bhk * gr.tiles_sink + tile) * (gr.nseg_sink - 1)
+                             : ((size_t)bhk * (gr.tiles - gr.tiles_sink) + (tile - gr.tiles_sink)) * (gr.nseg_band - 1);
+    float* dk = a.dk + ((size_t)bhk * L + key) * D + e4;
+    float* dv = a.dv + ((size_t)bhk * L + key) * D + e4;
+    f32x4 sk = *(const f32x4*)dk, sv = *(const f32x4*)dv;
+    for (int sg = 1; sg < nseg; ++sg) {
+        const float* slot = a.part + (base + sg - 1) * (size_t)(2 * 128 * D);
+        sk += *(const f32x4*)(slot + (size_t)(key - i0) * D + e4);
+        sv += *(const f32x4*)(slot + (size_t)(128 + key - i0) * D + e4);
     }
+    *(f32x4*)dk = sk;
+    *(f32x4*)dv = sv;
 }
 
 template <int D>
-hipError_t launch(const BackwardArgs& a, hipStream_t st) {
-    const int64_t ngr = (a.L + RW - 1) / RW;
-    const int64_t nq = (int64_t)a.B * a.Hq * ngr, nk = (int64_t)a.B * a.Hkv * ngr;
-    hipLaunchKernelGGL((bwd_q_kernel<D>), dim3((unsigned)((nq + BW - 1) / BW)), dim3(BT), 0, st, a);
+hipError_t launch(const BackwardArgs& a, const BwdGrid& gr, hipStream_t st) {
+    const int nqt = (int)((a.L + 127) / 128);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(a.B * a.Hq * nqt)), dim3(NT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_kv_kernel<D>), dim3((unsigned)((nk + BW - 1) / BW)), dim3(BT), 0, st, a);
+    const int64_t items = (int64_t)gr.bhkv * (gr.tiles_sink * gr.nseg_sink + (gr.tiles - gr.tiles_sink) * gr.nseg_band);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)items), dim3(NT), 0, st, a, gr);
     e = hipGetLastError();
-    if (e != hipSuccess || a.s == 0 || a.L <= a.r) return e;
-    const int32_t nseg = (int32_t)((a.L - a.r + kSinkSeg - 1) / kSinkSeg);
-    const int64_t nitems = (int64_t)a.B * a.Hkv * a.s * nseg;
-    hipLaunchKernelGGL((bwd_sink_kernel<D>), dim3((unsigned)((nitems + BW - 1) / BW)), dim3(BT), 0, st, a, nseg);
+    if (e != hipSuccess || gr.slots_band + gr.slots_sink == 0) return e;
+    const int64_t n = (int64_t)gr.bhkv * a.L * (D / 4);
+    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, gr);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_backward_bf16(const BackwardArgs& a, int d, hipStream_t st) {
-    if (d == 128) return launch<128>(a, st);
-    if (d == 64) return launch<64>(a, st);
+hipError_t launch_backward_bf16(const BackwardArgs& a, const BwdGrid& gr, int d, hipStream_t st) {
+    if (d == 128) return launch<128>(a, gr, st);
+    if (d == 64) return launch<64>(a, gr, st);
     return hipErrorInvalidValue;
 }
 

@@ -110,6 +110,25 @@ DilateLayout dilate_layout(const swa_desc* d, int64_t L, int64_t dil) {
     return x;
 }
 
+// Backward workspace: per-row log-sum-exp and D (each padded by a query
+// block's rows), then the partial dK/dV slots of split key tiles.
+struct BackwardLayout {
+    swa::BwdGrid grid{};
+    size_t lse2 = 0, dd = 0, part = 0, total = 0;
+};
+
+BackwardLayout backward_layout(const swa_desc* d, int64_t L) {
+    BackwardLayout x;
+    x.grid = swa::bwd_grid(d->B, d->Hq, d->Hkv, d->s, d->r, L);
+    const size_t rows = (size_t)d->B * d->Hq * (size_t)L + swa::kBwdStatPad;
+    x.lse2 = 0;
+    x.dd = round_up(rows * sizeof(float), 256);
+    x.part = x.dd + round_up(rows * sizeof(float), 256);
+    const size_t slots = (size_t)(x.grid.slots_band + x.grid.slots_sink);
+    x.total = x.part + round_up(slots * 2 * 128 * (size_t)d->d * sizeof(float), 256);
+    return x;
+}
+
 // Per-split partial results (max, sum, unnormalised O) per query head; one
 // split writes the output directly and needs none.
 size_t decode_ws_bytes(const swa_desc* desc, int32_t n_split) {
@@ -420,7 +439,7 @@ extern "C" {
 
 size_t swa_backward_workspace_bytes(const swa_desc* desc, int64_t L) {
     if (check_desc(desc, "swa_backward_workspace_bytes") != SWA_OK || L < 1 || L > kMaxPos) return 0;
-    return round_up((size_t)2 * desc->B * desc->Hq * (size_t)L * sizeof(float), 256);
+    return backward_layout(desc, L).total;
 }
 
 int swa_backward(const swa_desc* desc, const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -438,19 +457,18 @@ int swa_backward(const swa_desc* desc, const void* q, const void* k, const void*
         return st;
     if (L < 1) return fail(SWA_ERR_INVALID_ARG, "%s: L must be >= 1 (got %lld)", fn, (long long)L);
     if (L > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
-    const size_t rows = (size_t)desc->B * desc->Hq * (size_t)L;
-    const size_t need = round_up(2 * rows * sizeof(float), 256);
-    if (workspace_bytes < need)
-        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
-    // one wave per row (and per key, per sink segment), four per workgroup
-    if ((rows + 3) / 4 > 0x7fffffffULL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
-    if ((int64_t)(desc->Hq / desc->Hkv) * L > 0x7fffffffLL)
-        return fail(SWA_ERR_INVALID_ARG, "%s: L * (Hq / Hkv) beyond 2^31", fn);
-    if (desc->s > 0 && L > desc->r) {
-        const size_t sink_items = (size_t)desc->B * desc->Hkv * desc->s * ((L - desc->r + swa::kSinkSeg - 1) / swa::kSinkSeg);
-        if ((sink_items + 3) / 4 > 0x7fffffffULL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
-    }
+    const BackwardLayout lay = backward_layout(desc, L);
+    if (workspace_bytes < lay.total)
+        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
+    // grids: query tiles of 128 rows; dK/dV work items; 4-value groups of every key
+    const int64_t nqt = (L + 127) / 128;
+    const int64_t items = (int64_t)lay.grid.bhkv * ((int64_t)lay.grid.tiles_sink * lay.grid.nseg_sink +
+                                                    (int64_t)(lay.grid.tiles - lay.grid.tiles_sink) * lay.grid.nseg_band);
+    if ((int64_t)desc->B * desc->Hq * nqt > 0x7fffffffLL || items > 0x7fffffffLL ||
+        ((int64_t)lay.grid.bhkv * L * (desc->d / 4) + 255) / 256 > 0x7fffffffLL)
+        return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
 
+    char* ws = static_cast<char*>(workspace);
     swa::BackwardArgs a{};
     a.q = q;
     a.k = k;
@@ -460,8 +478,9 @@ int swa_backward(const swa_desc* desc, const void* q, const void* k, const void*
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    a.lse2 = static_cast<float*>(workspace);
-    a.dd = a.lse2 + rows;
+    a.lse2 = reinterpret_cast<float*>(ws + lay.lse2);
+    a.dd = reinterpret_cast<float*>(ws + lay.dd);
+    a.part = reinterpret_cast<float*>(ws + lay.part);
     a.L = L;
     a.B = desc->B;
     a.Hq = desc->Hq;
@@ -470,7 +489,7 @@ int swa_backward(const swa_desc* desc, const void* q, const void* k, const void*
     a.r = desc->r;
     a.scale = desc->scale;
     a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
-    return hip_status(swa::launch_backward_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
+    return hip_status(swa::launch_backward_bf16(a, lay.grid, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"
