@@ -141,6 +141,12 @@ struct Tile {
         return *(const bf16x8*)(t + off(swap23(l32), 2 * ks + g));
     }
 
+    // Column operand of k-step ks for MFMA column l32 (tile row l32, dims
+    // 16 ks + 8 g .. +7): the B operand of a product over the head dim.
+    static __device__ __forceinline__ bf16x8 colop(const char* t, int l32, int g, int ks) {
+        return *(const bf16x8*)(t + off(l32, 2 * ks + g));
+    }
+
     // Transposed operand [dim x row] of d-block db, k-step kk: lane (l32, g)
     // gets dim 32 db + l32 of tile rows 16 kk + 8 g .. +7.  ds_read_b64_tr_b16
     // hands lane 16q + 4a + j element e of the four values lane 16q + a + 4e
@@ -334,6 +340,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
     typedef Tile<D> TT;
     constexpr int KS = TT::KS, NDB = TT::NDB;
     __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TT::BYTES];
+    __shared__ __attribute__((aligned(1024))) char kvs[2][NW][TT::BYTES];   // the tile's K and V, 32 keys a wave
     __shared__ __attribute__((aligned(16))) float stat[NBUF][2][BLK];   // lse (log2 units), D
 
     const int lane = threadIdx.x & 63;
@@ -388,16 +395,16 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
     const __bf16* kg = (const __bf16*)a.k + (size_t)bhk * L * D;
     const __bf16* vg = (const __bf16*)a.v + (size_t)bhk * L * D;
 
-    // K^T and V^T B operands of S = Q K^T and dP = dO V^T (lane: its key, dims 16 ks + 8 g .. +7)
-    bf16x8 kB[KS], vB[KS];
-    {
-        const int kr = my_key < L ? my_key : L - 1;
+    // K and V of the tile's 128 keys stay in LDS for the whole item (the
+    // B operands of S = Q K^T and dP = dO V^T: lane takes its key, dims
+    // 16 ks + 8 g .. +7); keys past L are row L-1 (masked)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kB[ks] = *(const bf16x8*)(kg + (size_t)kr * D + 16 * ks + 8 * g);
-            vB[ks] = *(const bf16x8*)(vg + (size_t)kr * D + 16 * ks + 8 * g);
-        }
+    for (int w = 0; w < NW; ++w) {
+        TT::load(kvs[0][w], kg, i0 + 32 * w, 0, L - 1, wave, lane);
+        TT::load(kvs[1][w], vg, i0 + 32 * w, 0, L - 1, wave, lane);
     }
+    const char* Kw = kvs[0][wave];
+    const char* Vw = kvs[1][wave];
 
     // iteration it: query block qb = qb_lo + sb0 + it / G of q-head kvh * G + it % G
     auto issue = [&](int it, int buf) __attribute__((always_inline)) {
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
     }
     const float c = a.scale_log2e;
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K and V are in registers
+    // (the first wait below also covers the K and V loads, issued before)
     issue(0, 0);
     if (niter > 1) issue(1, 1);
     int buf = 0;
@@ -444,29 +451,24 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
             f32x16 sa = {}, pa = {};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                sa = mfma(TT::rowop(Qt, l32, g, ks), kB[ks], sa);
-                pa = mfma(TT::rowop(Ot, l32, g, ks), vB[ks], pa);
+                sa = mfma(TT::rowop(Qt, l32, g, ks), TT::colop(Kw, l32, g, ks), sa);
+                pa = mfma(TT::rowop(Ot, l32, g, ks), TT::colop(Vw, l32, g, ks), pa);
             }
-            // lse and D of this lane's 16 queries (rows 8g .. 8g+7, 16+8g .. +7)
-            const f32x4* ls = (const f32x4*)&stat[buf][0][0];
-            const f32x4* dd = (const f32x4*)&stat[buf][1][0];
-            f32x4 lq[4], dq4[4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    lq[2 * h + u] = ls[(16 * h + 8 * g) / 4 + u];
-                    dq4[2 * h + u] = dd[(16 * h + 8 * g) / 4 + u];
-                }
+            // lse and D of this lane's 16 queries (rows 8g .. 8g+7, 16+8g .. +7),
+            // four at a time: element i takes lq(i) = stat[.][16 (i/8) + 8 g + i%8]
+            const float* ls = &stat[buf][0][0];
+            const float* dd = &stat[buf][1][0];
+            auto lq = [&](int i) __attribute__((always_inline)) { return ls[crow(i, g)]; };
+            auto dq4 = [&](int i) __attribute__((always_inline)) { return dd[crow(i, g)]; };
             const bool full = kw0 + BLK - 1 <= tq0 && tq0 + BLK - 1 <= L - 1 && kw0 + BLK - 1 <= L - 1 &&
                               (kw0 + BLK - 1 < s || kw0 >= tq0 + BLK - 1 - r + 1);
             bf16x8 pp[2], ps[2];
             if (full) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq[i / 4][i % 4]));
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq(i)));
                     pp[i / 8][i % 8] = (__bf16)p;
-                    ps[i / 8][i % 8] = (__bf16)(p * (pa[i] - dq4[i / 4][i % 4]));
+                    ps[i / 8][i % 8] = (__bf16)(p * (pa[i] - dq4(i)));
                 }
             } else {
                 // masked pairs (and rows past L, whose statistics are not
@@ -475,8 +477,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
                 for (int i = 0; i < 16; ++i) {
                     const int t = tq0 + crow(i, g);
                     const bool ok = (t <= L - 1) & (my_key <= L - 1) & in_set(t, my_key, s, r);
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq[i / 4][i % 4]));
-                    const float dsv = p * (pa[i] - dq4[i / 4][i % 4]);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq(i)));
+                    const float dsv = p * (pa[i] - dq4(i));
                     pp[i / 8][i % 8] = (__bf16)(ok ? p : 0.0f);
                     ps[i / 8][i % 8] = (__bf16)(ok ? dsv : 0.0f);
                 }
