@@ -44,13 +44,13 @@ def _load():
         vp = ctypes.c_void_p
         lib.swa_oracle_rows.restype = ctypes.c_int
         lib.swa_oracle_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, f64, f64, i64,
-                                        i64, vp, vp, vp, i64]
+                                        i64, vp, vp, vp, i64, vp, i64]
         lib.swa_oracle_attend_set.restype = ctypes.c_int
         lib.swa_oracle_attend_set.argtypes = [vp, vp, vp, i64, i64, f64, vp]
         lib.swa_oracle_rope.restype = ctypes.c_int
         lib.swa_oracle_rope.argtypes = [vp, vp, i64, i64, f64]
         lib.swa_oracle_key_set.restype = i64
-        lib.swa_oracle_key_set.argtypes = [i64, i64, i64, i64, vp]
+        lib.swa_oracle_key_set.argtypes = [i64, i64, i64, i64, vp, i64, vp]
         lib.swa_oracle_threads.restype = ctypes.c_int
         lib.swa_oracle_threads.argtypes = []
         _lib = lib
@@ -70,11 +70,19 @@ def threads() -> int:
     return int(_load().swa_oracle_threads())
 
 
-def key_set(t: int, s: int, r: int, dilation: int = 1) -> np.ndarray:
+def _globals(globals_):
+    g = np.ascontiguousarray(np.zeros(0) if globals_ is None else globals_, dtype=np.int64)
+    return g, (_ptr(g) if g.size else None), int(g.size)
+
+
+def key_set(t: int, s: int, r: int, dilation: int = 1, globals_=None) -> np.ndarray:
     """U(t) as the oracle enumerates it (sinks, then the window; with a
-    dilation the window takes every dilation-th position back from t)."""
-    buf = np.empty(s + r, dtype=np.int64)
-    n = _load().swa_oracle_key_set(t, s, r, dilation, _ptr(buf))
+    dilation the window takes every dilation-th position back from t; with
+    global positions, a global row takes 0..t and other rows add the global
+    positions <= t)."""
+    g, gp, ng = _globals(globals_)
+    buf = np.empty(max(s + r + ng, t + 1), dtype=np.int64)
+    n = _load().swa_oracle_key_set(t, s, r, dilation, gp, ng, _ptr(buf))
     if n < 0:
         raise ValueError("invalid key-set arguments")
     return buf[:n].copy()
@@ -90,8 +98,12 @@ def rope(x, pos: int, base: float) -> np.ndarray:
 
 
 def prefill_rows(q, k, v, s: int, r: int, *, scale: float | None = None, rope_base: float = 0.0,
-                 qpos0: int = 0, rows=None, return_nkeys: bool = False, dilation: int = 1):
+                 qpos0: int = 0, rows=None, return_nkeys: bool = False, dilation: int = 1, globals_=None):
     """Attention rows over the sink + recent key set, fp64.
+
+    ``globals_``: sorted, distinct global-token positions (plain window only):
+    a row in it attends keys 0..t, any other row adds the global positions
+    up to itself to U(t).
 
     q: [B, Hq, Lq, d] (row i at position qpos0 + i); k, v: [B, Hkv, Lk, d]
     (row p at position p).  ``rows``: int array [n, 3] of (b, h, i); None means
@@ -110,9 +122,10 @@ def prefill_rows(q, k, v, s: int, r: int, *, scale: float | None = None, rope_ba
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
     out = np.empty((rows.shape[0], d), dtype=np.float64)
     nk = np.empty(rows.shape[0], dtype=np.int64)
+    g, gp, ng = _globals(globals_)
     rc = _load().swa_oracle_rows(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Lq, Lk, d, s, r, float(scale),
                                  float(rope_base), qpos0, rows.shape[0], _ptr(rows), _ptr(out), _ptr(nk),
-                                 int(dilation))
+                                 int(dilation), gp, ng)
     if rc != 0:
         raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
     return (out, nk) if return_nkeys else out

@@ -21,6 +21,12 @@
  *    positions skip delta - 1 tokens, same count, wider reach); the sinks
  *    are unchanged and a key in both sets counts once.  delta = 1 is U(t).
  *
+ *    With task-bound global tokens (a sorted list G of positions; the
+ *    Longformer section and the glossary entry on global tokens of that
+ *    page: a few tokens visible to the whole sequence, and seeing all of it),
+ *    in causal form: a row t in G attends every key <= t; any other row
+ *    attends U(t) plus the global positions g <= t, each key once.
+ *
  *  - Scores and normalisation.  x_i = (q_t . k_i) / sqrt(d) (here: times the
  *    caller's scale), then softmax over U(t) and the weighted sum of values:
  *    eq:attn-fixed-softmax-sink on the t6page page, eq.(1) of section 2.1 of
@@ -48,18 +54,44 @@
 #define ORACLE_EINVAL -1
 #define ORACLE_ENOMEM -2
 
-/* Number of keys in U(t) and the list itself, sinks first, then the window,
- * which together are in increasing (temporal) order. */
-static int64_t key_set(int64_t t, int64_t s, int64_t r, int64_t dil, int64_t* keys) {
+/* Whether position t is in the sorted list G (ng entries). */
+static int is_global(int64_t t, const int64_t* G, int64_t ng) {
+    for (int64_t j = 0; j < ng; ++j)
+        if (G[j] == t) return 1;
+    return 0;
+}
+
+/* Number of keys in U(t) and the list itself, in increasing (temporal)
+ * order: the sinks, then (with global tokens) the global positions between
+ * the sinks and the window, then the window.  A global row takes 0 .. t.
+ * Global tokens are defined for the plain window (dil = 1). */
+static int64_t key_set(int64_t t, int64_t s, int64_t r, int64_t dil, const int64_t* G, int64_t ng, int64_t* keys) {
     int64_t n = 0;
+    if (ng > 0 && is_global(t, G, ng)) {
+        for (int64_t j = 0; j <= t; ++j) keys[n++] = j;
+        return n;
+    }
     int64_t ns = s < t + 1 ? s : t + 1;
     for (int64_t j = 0; j < ns; ++j) keys[n++] = j;
+    /* global positions >= s and before the window (those in the window or
+       among the sinks are already in the set) */
+    int64_t win_lo = t - r + 1 > s ? t - r + 1 : s;
+    for (int64_t j = 0; j < ng; ++j)
+        if (G[j] >= s && G[j] < win_lo && G[j] <= t) keys[n++] = G[j];
     /* window positions t - dil*m, m = r-1 .. 0 (increasing), those >= s */
     for (int64_t m = r - 1; m >= 0; --m) {
         int64_t i = t - dil * m;
         if (i >= s && i >= 0) keys[n++] = i;
     }
     return n;
+}
+
+/* G must be strictly increasing, positions >= 0. */
+static int globals_ok(const int64_t* G, int64_t ng) {
+    if (ng < 0 || (ng > 0 && !G)) return 0;
+    for (int64_t j = 0; j < ng; ++j)
+        if (G[j] < 0 || (j > 0 && G[j] <= G[j - 1])) return 0;
+    return 1;
 }
 
 /* Rotation angles.  Position p turns pair j by p * theta_j with
@@ -109,17 +141,20 @@ static void rope_rotate(const rope_table* T, const double* x, double* y, int64_t
 int swa_oracle_rows(const float* q, const float* k, const float* v,
                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk, int64_t d,
                     int64_t s, int64_t r, double scale, double rope_base, int64_t qpos0,
-                    int64_t nrows, const int64_t* rows, double* out, int64_t* nkeys, int64_t dil) {
+                    int64_t nrows, const int64_t* rows, double* out, int64_t* nkeys, int64_t dil,
+                    const int64_t* G, int64_t ng) {
     if (!q || !k || !v || !rows || !out) return ORACLE_EINVAL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || r < 1 || s < 0 || qpos0 < 0 || dil < 1)
         return ORACLE_EINVAL;
     if (rope_base > 0 && (d % 2)) return ORACLE_EINVAL;
+    if (!globals_ok(G, ng) || (ng > 0 && (rope_base > 0 || dil != 1))) return ORACLE_EINVAL;
     for (int64_t n = 0; n < nrows; ++n) {
         int64_t b = rows[3 * n], h = rows[3 * n + 1], i = rows[3 * n + 2];
         if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Lq || qpos0 + i >= Lk) return ORACLE_EINVAL;
     }
     int64_t group = Hq / Hkv;
-    int64_t maxkeys = s + r;
+    int64_t maxkeys = s + r + ng;
+    if (ng > 0 && maxkeys < Lk) maxkeys = Lk;   /* a global row takes 0 .. t */
     int failed = 0;
     rope_table T = {0, 0, NULL, NULL};
     if (rope_base > 0 && rope_table_init(&T, maxkeys, d, rope_base) != ORACLE_OK) return ORACLE_ENOMEM;
@@ -146,7 +181,7 @@ int swa_oracle_rows(const float* q, const float* k, const float* v,
                 const float* kbase = k + (b * Hkv + kvh) * Lk * d;
                 const float* vbase = v + (b * Hkv + kvh) * Lk * d;
 
-                int64_t nk = key_set(t, s, r, dil, keys);
+                int64_t nk = key_set(t, s, r, dil, G, ng, keys);
                 if (nkeys) nkeys[n] = nk;
 
                 for (int64_t e = 0; e < d; ++e) qd[e] = (double)qrow[e];
@@ -231,10 +266,12 @@ int swa_oracle_rope(const double* x, double* y, int64_t d, int64_t pos, double b
     return ORACLE_OK;
 }
 
-/* |U(t)| and the key list, exposed for the key-set pins. */
-int64_t swa_oracle_key_set(int64_t t, int64_t s, int64_t r, int64_t dil, int64_t* keys) {
-    if (t < 0 || s < 0 || r < 1 || dil < 1 || !keys) return ORACLE_EINVAL;
-    return key_set(t, s, r, dil, keys);
+/* |U(t)| and the key list, exposed for the key-set pins; keys must hold
+ * s + r + ng entries, or t + 1 if that is more. */
+int64_t swa_oracle_key_set(int64_t t, int64_t s, int64_t r, int64_t dil, const int64_t* G, int64_t ng, int64_t* keys) {
+    if (t < 0 || s < 0 || r < 1 || dil < 1 || !keys || !globals_ok(G, ng) || (ng > 0 && dil != 1))
+        return ORACLE_EINVAL;
+    return key_set(t, s, r, dil, G, ng, keys);
 }
 
 /* Threads the parallel loops use (the CPU-baseline leg reports it). */
