@@ -145,6 +145,28 @@ int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, c
                         int64_t L, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Task-bound global tokens on the sliding window with sinks (the Longformer
+ * section and the glossary entry on global tokens of the t6page page
+ * "滑窗与固定稀疏": a few tokens, chosen by the task, see the whole sequence
+ * and are seen by all of it), in causal form.  globals: ng HOST positions
+ * (0 <= ng <= SWA_MAX_GLOBALS), strictly increasing, each in 0 .. L-1.  A row
+ * t in globals attends every key 0 .. t; any other row attends U(t) plus the
+ * global positions g <= t, each key once (a global among the sinks or inside
+ * the window adds nothing).  Layouts as for swa_prefill without a cache;
+ * bf16, no RoPE, up to 16 q-heads per kv-head.  ng = 0 is swa_prefill.
+ * Runs the banded prefill, then merges each row with its global keys through
+ * the two softmax normalisers, then computes the global rows as dense
+ * causal rows.  Workspace: swa_prefill_global_workspace_bytes(desc, L, ng)
+ * bytes (global keys and values, the rows' log-sum-exp, split partials).
+ * Errors: those of swa_prefill, SWA_ERR_INVALID_ARG for bad globals or a
+ * short workspace, SWA_ERR_UNSUPPORTED for fp32, RoPE or wide GQA groups.
+ */
+#define SWA_MAX_GLOBALS 64
+size_t swa_prefill_global_workspace_bytes(const swa_desc* desc, int64_t L, int32_t ng);
+int swa_prefill_global(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
+                       const int32_t* globals, int32_t ng, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-K decode.  Bytes of workspace swa_decode needs for n_split splits of
  * the s + r slots (0 = the library's choice for this shape):
  * B * Hq * n_split * (d + 2) * 4 bytes, or 0 for one split (the split

@@ -8,6 +8,8 @@ of include/swa.h); this package binds it for PyTorch callers:
   * prefill_dilated(q, k, v, s, r, dilation) the same with a dilated window
   * rope_keys(k, pos0, base)           keys rotated at their positions (the
                                        form every RoPE call takes)
+  * prefill_global(q, k, v, s, r, globals) the same with task-bound global
+                                       tokens
   * cache_append(k, v, kc, vc, pos0, ...) write tokens into the rolling cache
   * decode(q, kc, vc, T, s, r, ...)    split-K single-query decode
   * decode_step(q, k, v, kc, vc, T, s, r, ...) append token T-1 and decode
@@ -30,6 +32,7 @@ from .ops import (  # noqa: F401
     new_cache,
     prefill,
     prefill_dilated,
+    prefill_global,
     prefill_workspace_bytes,
     rope_keys,
 )

@@ -23,7 +23,7 @@ SWA_BF16 = 1
 EXPORTS = (
     "swa_prefill_workspace_bytes", "swa_rope_keys", "swa_prefill", "swa_cache_append", "swa_decode_workspace_bytes",
     "swa_decode", "swa_decode_step", "swa_decode_step_noalloc", "swa_decode_default_splits", "swa_prefill_dilated_workspace_bytes",
-    "swa_prefill_dilated", "swa_backward_workspace_bytes", "swa_backward", "swa_status_str", "swa_last_error",
+    "swa_prefill_dilated", "swa_prefill_global_workspace_bytes", "swa_prefill_global", "swa_backward_workspace_bytes", "swa_backward", "swa_status_str", "swa_last_error",
     "swa_abi_version",
 )
 
@@ -76,6 +76,10 @@ def load() -> ctypes.CDLL:
     lib.swa_prefill_dilated_workspace_bytes.restype = sz
     lib.swa_prefill_dilated.argtypes = [dp, i32, vp, vp, vp, vp, i64, vp, sz, vp]
     lib.swa_prefill_dilated.restype = ctypes.c_int
+    lib.swa_prefill_global_workspace_bytes.argtypes = [dp, i64, i32]
+    lib.swa_prefill_global_workspace_bytes.restype = sz
+    lib.swa_prefill_global.argtypes = [dp, vp, vp, vp, vp, i64, ctypes.POINTER(ctypes.c_int32), i32, vp, sz, vp]
+    lib.swa_prefill_global.restype = ctypes.c_int
     lib.swa_backward_workspace_bytes.argtypes = [dp, i64]
     lib.swa_backward_workspace_bytes.restype = sz
     lib.swa_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz, vp]
@@ -149,6 +153,21 @@ def swa_prefill_dilated_workspace_bytes(desc: SwaDesc, L: int, dilation: int) ->
 
 def swa_prefill_dilated(desc, dilation, q, k, v, o, L, workspace, workspace_bytes, stream) -> int:
     return load().swa_prefill_dilated(ctypes.byref(desc), dilation, q, k, v, o, L, workspace, workspace_bytes, stream)
+
+
+MAX_GLOBALS = 64   # SWA_MAX_GLOBALS of include/swa.h
+
+
+def swa_prefill_global_workspace_bytes(desc: SwaDesc, L: int, ng: int) -> int:
+    return load().swa_prefill_global_workspace_bytes(ctypes.byref(desc), L, ng)
+
+
+def swa_prefill_global(desc, q, k, v, o, L, globals_, ng, workspace, workspace_bytes, stream) -> int:
+    """globals_: a sequence of host positions (ints) or None."""
+    arr = None
+    if globals_ is not None:
+        arr = (ctypes.c_int32 * max(1, len(globals_)))(*[int(x) for x in globals_])
+    return load().swa_prefill_global(ctypes.byref(desc), q, k, v, o, L, arr, ng, workspace, workspace_bytes, stream)
 
 
 def swa_backward_workspace_bytes(desc: SwaDesc, L: int) -> int:

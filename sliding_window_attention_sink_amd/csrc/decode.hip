@@ -163,7 +163,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
         const bool qband = col < G;
         const bool qsink = rope && col >= G && col < 2 * G;
         const int head = qband ? col : (qsink ? col - G : 0);
-        const __bf16* qrow = (const __bf16*)a.q + ((size_t)b * a.Hq + kvh * G + head) * D;
+        const __bf16* qrow = (const __bf16*)a.q + ((size_t)b * a.Hq + kvh * G + head) * a.qo_stride;
         u32x4 x[KSTEPS];
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
         }
         if (a.n_split == 1) {
             // one split: this workgroup saw every slot, so it finishes the head
-            ((__bf16*)a.o)[((size_t)b * a.Hq + kvh * G + cl) * D + dim] = (__bf16)(o / l);
+            ((__bf16*)a.o)[((size_t)b * a.Hq + kvh * G + cl) * a.qo_stride + dim] = (__bf16)(o / l);
             continue;
         }
         float* ws = a.ws + (((size_t)b * a.Hq + kvh * G + cl) * a.n_split + split) * (D + 2);
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
         l += f * ws[k * (D + 2) + 1];
         o += f * ws[k * (D + 2) + 2 + dim];
     }
-    ((__bf16*)a.o)[(size_t)bh * D + dim] = (__bf16)(o / l);
+    ((__bf16*)a.o)[(size_t)bh * a.qo_stride + dim] = (__bf16)(o / l);
 }
 
 template <int D>

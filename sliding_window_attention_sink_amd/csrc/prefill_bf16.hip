@@ -782,6 +782,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     static_assert(PW * WROWS * T::ORS <= (int)sizeof(smem), "output staging fits the tile buffers");
     T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * D, oacc,
                my_valid ? 1.0f / l_tot : 0.0f, lane, tw1 - tw0 + 1);
+    if (a.lse != nullptr && my_valid && g == 0) a.lse[qoff / D] = m_c + __builtin_amdgcn_logf(l_tot);
 }
 
 template <int D>

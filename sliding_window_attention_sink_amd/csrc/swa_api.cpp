@@ -159,10 +159,13 @@ size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L) {
     return 0;
 }
 
-int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
-                const void* k_cache, const void* v_cache, int64_t pos0, void* workspace, size_t workspace_bytes,
-                void* stream) {
-    static const char* fn = "swa_prefill";
+}  // extern "C"
+
+namespace {
+
+// swa_prefill; lse (null or [B, Hq, L]) receives each row's log2-sum-exp.
+int prefill_impl(const char* fn, const swa_desc* desc, const void* q, const void* k, const void* v, void* o,
+                 int64_t L, const void* k_cache, const void* v_cache, int64_t pos0, float* lse, void* stream) {
     clear_error();
     int st = check_desc(desc, fn);
     if (st) return st;
@@ -178,8 +181,6 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
     } else if (pos0 != 0) {
         return fail(SWA_ERR_INVALID_ARG, "%s: pos0 > 0 needs the rolling cache", fn);
     }
-    (void)workspace;
-    (void)workspace_bytes;
     const bool rope = desc->rope_base > 0.0f;
     const bool bf16 = desc->dtype == SWA_BF16;
     const int64_t rows_per_block =
@@ -213,8 +214,21 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
         a.merge_sink = 0;
         a.rope_rr = rope_rr(desc);
     }
+    a.lse = lse;
     hipError_t e = bf16 ? swa::launch_prefill_bf16(a, desc->d, hs) : swa::launch_prefill_f32(a, desc->d, hs);
     return hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
+                const void* k_cache, const void* v_cache, int64_t pos0, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    (void)workspace;         // no prefill kernel uses one (swa_prefill_workspace_bytes is 0)
+    (void)workspace_bytes;
+    return prefill_impl("swa_prefill", desc, q, k, v, o, L, k_cache, v_cache, pos0, nullptr, stream);
 }
 
 int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new, int64_t n, int64_t pos0,
@@ -268,6 +282,132 @@ int swa_rope_keys(const swa_desc* desc, const void* k, int64_t n, int64_t pos0, 
     a.pos0 = pos0;
     a.rope_rr = rope_rr(desc);
     return hip_status(swa::launch_rope_keys_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of swa_prefill_global: gathered global keys and values, the
+// banded rows' log-sum-exp, and the split partials of the dense global rows.
+struct GlobalLayout {
+    swa_desc dense{};
+    int32_t n_split = 1;
+    size_t kg = 0, vg = 0, lse = 0, part = 0, total = 0;
+};
+
+GlobalLayout global_layout(const swa_desc* d, int64_t L) {
+    GlobalLayout x;
+    // the rows in G attend keys 0 .. t: the decode over a "cache" of L slots
+    // with L-1 sink slots and one rolling slot, which holds exactly keys
+    // 0 .. T-1 for T <= L
+    x.dense = *d;
+    x.dense.s = (int32_t)(L - 1);
+    x.dense.r = 1;
+    x.n_split = default_splits(&x.dense);
+    const size_t kgb = (size_t)d->B * d->Hkv * swa::kMaxGlobals * d->d * 2;
+    x.kg = 0;
+    x.vg = round_up(kgb, 256);
+    x.lse = x.vg + round_up(kgb, 256);
+    x.part = x.lse + round_up((size_t)d->B * d->Hq * (size_t)L * sizeof(float), 256);
+    x.total = x.part + round_up(decode_ws_bytes(&x.dense, x.n_split), 256);
+    return x;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t swa_prefill_global_workspace_bytes(const swa_desc* desc, int64_t L, int32_t ng) {
+    if (check_desc(desc, "swa_prefill_global_workspace_bytes") != SWA_OK || L < 1 || L > kMaxPos) return 0;
+    if (ng < 1 || ng > swa::kMaxGlobals) return 0;
+    return global_layout(desc, L).total;
+}
+
+int swa_prefill_global(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
+                       const int32_t* globals, int32_t ng, void* workspace, size_t workspace_bytes, void* stream) {
+    static const char* fn = "swa_prefill_global";
+    clear_error();
+    int st = check_desc(desc, fn);
+    if (st) return st;
+    if (desc->dtype != SWA_BF16) return fail(SWA_ERR_UNSUPPORTED, "%s: global tokens are built for bf16", fn);
+    if (desc->rope_base > 0.0f) return fail(SWA_ERR_UNSUPPORTED, "%s: global tokens with RoPE are not built", fn);
+    if (desc->Hq / desc->Hkv > 16) return fail(SWA_ERR_UNSUPPORTED, "%s: more than 16 q-heads per kv-head", fn);
+    if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k, fn, "k")) || (st = check_ptr(v, fn, "v")) ||
+        (st = check_ptr(o, fn, "o")))
+        return st;
+    if (L < 1) return fail(SWA_ERR_INVALID_ARG, "%s: L must be >= 1 (got %lld)", fn, (long long)L);
+    if (L > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
+    if (ng < 0 || ng > swa::kMaxGlobals)
+        return fail(SWA_ERR_INVALID_ARG, "%s: %d global tokens (0 .. %d)", fn, ng, swa::kMaxGlobals);
+    if (ng > 0 && globals == nullptr) return fail(SWA_ERR_INVALID_ARG, "%s: globals is NULL", fn);
+    for (int32_t j = 0; j < ng; ++j) {
+        if (globals[j] < 0 || globals[j] >= L)
+            return fail(SWA_ERR_INVALID_ARG, "%s: global position %d outside 0 .. L-1", fn, globals[j]);
+        if (j > 0 && globals[j] <= globals[j - 1])
+            return fail(SWA_ERR_INVALID_ARG, "%s: global positions must increase strictly", fn);
+    }
+    if (ng == 0) return swa_prefill(desc, q, k, v, o, L, nullptr, nullptr, 0, nullptr, 0, stream);
+    const GlobalLayout lay = global_layout(desc, L);
+    if ((st = check_ptr(workspace, fn, "workspace"))) return st;
+    if (workspace_bytes < lay.total)
+        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
+    if ((int64_t)desc->B * desc->Hq * ((L + 127) / 128) > 0x7fffffffLL) return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    swa::GlobalArgs ga{};
+    ga.q = q;
+    ga.k = k;
+    ga.v = v;
+    ga.o = o;
+    ga.kg = ws + lay.kg;
+    ga.vg = ws + lay.vg;
+    ga.lse = reinterpret_cast<const float*>(ws + lay.lse);
+    ga.L = L;
+    ga.B = desc->B;
+    ga.Hq = desc->Hq;
+    ga.Hkv = desc->Hkv;
+    ga.s = desc->s;
+    ga.r = desc->r;
+    ga.ng = ng;
+    ga.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
+    for (int32_t j = 0; j < ng; ++j) ga.pos[j] = globals[j];
+    if ((st = hip_status(swa::launch_global_gather_bf16(ga, desc->d, hs), fn))) return st;
+    // the banded rows, with their log-sum-exp
+    if ((st = prefill_impl(fn, desc, q, k, v, o, L, nullptr, nullptr, 0, reinterpret_cast<float*>(ws + lay.lse),
+                           stream)))
+        return st;
+    if ((st = hip_status(swa::launch_global_merge_bf16(ga, desc->d, hs), fn))) return st;
+    // the global rows: dense causal rows over keys 0 .. t
+    const int S = (int)L;
+    int sps = (S + lay.n_split - 1) / lay.n_split;
+    sps = (sps + 31) / 32 * 32;
+    for (int32_t j = 0; j < ng; ++j) {
+        const int64_t t = globals[j];
+        swa::DecodeArgs da{};
+        da.q = static_cast<const __bf16*>(q) + t * desc->d;
+        da.kc = k;
+        da.vc = v;
+        da.o = static_cast<__bf16*>(o) + t * desc->d;
+        da.ws = reinterpret_cast<float*>(ws + lay.part);
+        da.kn = nullptr;
+        da.vn = nullptr;
+        da.T = t + 1;
+        da.j_new = -1;
+        da.rope_rr = 0.0;
+        da.qo_stride = L * desc->d;
+        da.B = desc->B;
+        da.Hq = desc->Hq;
+        da.Hkv = desc->Hkv;
+        da.s = lay.dense.s;
+        da.r = lay.dense.r;
+        da.n_split = lay.n_split;
+        da.slots_per_split = sps;
+        da.scale_log2e = ga.scale_log2e;
+        if ((st = hip_status(swa::launch_decode_bf16(da, desc->d, hs), fn))) return st;
+    }
+    return SWA_OK;
 }
 
 size_t swa_prefill_dilated_workspace_bytes(const swa_desc* desc, int64_t L, int32_t dilation) {
@@ -384,6 +524,7 @@ int decode_impl(const char* fn, const swa_desc* desc, const void* q, const void*
     a.slots_per_split = sps;
     a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
     a.rope_rr = desc->rope_base > 0.0f ? rope_rr(desc) : 0.0;
+    a.qo_stride = desc->d;
     return hip_status(swa::launch_decode_bf16(a, desc->d, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 

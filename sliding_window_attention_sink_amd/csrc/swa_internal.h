@@ -32,6 +32,9 @@ struct PrefillArgs {
     // token's position; the kernel rotates the queries, at t for window keys
     // and at min(t, s+r-1) for sinks.  rope_rr = base^(-2/d).
     double rope_rr;
+    // null, or [B, Hq, L]: each row's log2-sum-exp of its scaled scores
+    // (scale * log2(e) units), for merging further keys into the row
+    float* lse;
 };
 
 struct AppendArgs {
@@ -57,6 +60,7 @@ struct DecodeArgs {
     int64_t T;          // tokens in the cache including the current one
     int32_t j_new;      // cache slot of token T-1 with kn/vn, else -1
     double rope_rr;     // RoPE: base^(-2/d) (cache keys stored rotated at their position); 0 = no RoPE
+    int64_t qo_stride;  // elements between the (batch, q-head) rows of q and of o (d for [B, Hq, d])
     int32_t B, Hq, Hkv, s, r;
     int32_t n_split;
     int32_t slots_per_split;
@@ -71,6 +75,25 @@ struct RopeKeysArgs {
     int64_t rows, n, pos0;
     double rope_rr;     // base^(-2/d)
 };
+
+// Task-bound global tokens (swa_prefill_global): at most kMaxGlobals sorted
+// positions, passed by value.
+constexpr int kMaxGlobals = 64;
+struct GlobalArgs {
+    const void* q;      // [B, Hq, L, d]
+    const void* k;      // [B, Hkv, L, d]
+    const void* v;
+    void* o;            // [B, Hq, L, d]: the banded rows, merged in place
+    void* kg;           // workspace [B * Hkv, kMaxGlobals, d]: keys of the global positions
+    void* vg;           // ... values
+    const float* lse;   // [B, Hq, L]: the banded rows' log2-sum-exp (scale * log2(e) units)
+    int64_t L;
+    int32_t B, Hq, Hkv, s, r, ng;
+    float scale_log2e;
+    int32_t pos[kMaxGlobals];
+};
+hipError_t launch_global_gather_bf16(const GlobalArgs& a, int d, hipStream_t st);
+hipError_t launch_global_merge_bf16(const GlobalArgs& a, int d, hipStream_t st);
 
 // Query rows per workgroup of the bf16 prefill kernel for this head layout.
 int prefill_bf16_rows_per_block(int Hq, int Hkv);

@@ -118,6 +118,28 @@ def prefill_dilated(q, k, v, s, r, dilation, *, scale=None, out=None, workspace=
     return out
 
 
+def prefill_global(q, k, v, s, r, globals_, *, scale=None, out=None, workspace=None, stream=None):
+    """Prefill with task-bound global tokens at the given positions (host ints,
+    strictly increasing): those rows attend every earlier key, every other
+    row also attends the global positions up to itself."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale)
+    _need(k, "k", (B, Hkv, L, d), q.dtype, dev)
+    _need(v, "v", (B, Hkv, L, d), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.shape, q.dtype, dev)
+    g = [int(x) for x in globals_]
+    wsb = _lib.swa_prefill_global_workspace_bytes(desc, L, len(g)) if g else 0
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    check(_lib.swa_prefill_global(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(out), L, g, len(g), _ptr(workspace),
+                                  0 if workspace is None else workspace.numel(), _stream(dev, stream)))
+    return out
+
+
 def backward(q, k, v, o, dout, s, r, *, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Gradients (dq, dk, dv; fp32) of prefill's rows for the upstream dout.
 

@@ -173,7 +173,16 @@ def test_prefill_dilated_rejects():
 def test_backward_rejects():
     d_ = desc()
     wsb = _lib.swa_backward_workspace_bytes(d_, 100)
-    assert wsb == 2 * 1 * 4 * 100 * 4 + 256 - (2 * 1 * 4 * 100 * 4) % 256   # two floats a row, 256-byte rounded
+    # two floats a row (log-sum-exp and D), each array padded by 64 rows and
+    # rounded to 256 bytes; no split key tile at L = 100
+    per = (1 * 4 * 100 + 64) * 4
+    assert wsb == 2 * ((per + 255) // 256 * 256)
+    # split tiles add partial slots of 2 * 128 * d floats: GQA 4/2 (256 / 2 =
+    # 128 query blocks a segment), L = 8192, r = 4096 -> band tiles of
+    # (126 + 4096) // 32 + 1 = 132 blocks in 2 segments, 64 tiles, 2 kv-heads
+    big = desc(s=0, r=4096)
+    per = (1 * 4 * 8192 + 64) * 4
+    assert _lib.swa_backward_workspace_bytes(big, 8192) == 2 * ((per + 255) // 256 * 256) + 2 * 64 * 1 * 2 * 128 * 128 * 4
     G1, G2, G3 = 0x80000, 0x90000, 0xA0000
 
     def bwd(dd=d_, q=A, dq=G1, ws=W, n=wsb, L=100):
@@ -215,3 +224,25 @@ def test_decode_step_noalloc_rejects_on_host(lib):
     assert _lib.swa_decode_step_noalloc(desc(), A, B_, C, D, E, 100, F, 65, None) == _lib.SWA_ERR_INVALID_ARG
     assert _lib.swa_decode_step_noalloc(desc(dtype=_lib.SWA_F32), A, B_, C, D, E, 100, F, 2, None) == \
         _lib.SWA_ERR_UNSUPPORTED
+
+
+def test_prefill_global_rejects():
+    d_ = desc()
+    wsb = _lib.swa_prefill_global_workspace_bytes(d_, 100, 3)
+    assert wsb > 0 and _lib.swa_prefill_global_workspace_bytes(d_, 100, 0) == 0
+    assert _lib.swa_prefill_global_workspace_bytes(d_, 100, 65) == 0
+
+    def glob(dd=d_, G=(5, 9, 40), ng=None, ws=W, n=wsb, L=100):
+        return _lib.swa_prefill_global(dd, A, B_, C, D, L, G, len(G) if ng is None else ng, ws, n, None)
+
+    assert glob(G=(5, 5)) == -1 and "increase" in _lib.swa_last_error()
+    assert glob(G=(9, 5)) == -1 and "increase" in _lib.swa_last_error()
+    assert glob(G=(5, 100)) == -1 and "outside" in _lib.swa_last_error()
+    assert glob(G=(-1, 5)) == -1 and "outside" in _lib.swa_last_error()
+    assert glob(G=None, ng=2) == -1 and "globals is NULL" in _lib.swa_last_error()
+    assert glob(G=tuple(range(65)), L=200) == -1 and "global tokens" in _lib.swa_last_error()
+    assert glob(ws=None) == -1 and "workspace" in _lib.swa_last_error()
+    assert glob(n=wsb - 16) == -1 and "workspace" in _lib.swa_last_error()
+    assert glob(dd=desc(dtype=_lib.SWA_F32)) == -2
+    assert glob(dd=desc(rope_base=1e4)) == -2
+    assert glob(dd=desc(Hq=34, Hkv=2)) == -2
