@@ -308,6 +308,41 @@ def bench_dilated(torch, swa, w, dilations, steps=10, settle=_no_settle):
     return res
 
 
+def global_key_count_sum(L: int, s: int, r: int, G) -> int:
+    """sum over rows of |U_G(t)|: a global row t has t + 1 keys, any other row
+    min(t+1, s+r) plus the global positions in [s, t-r+1) that are <= t."""
+    t = np.arange(L, dtype=np.int64)
+    n = np.minimum(t + 1, s + r)
+    gs = np.asarray(G, dtype=np.int64)
+    lo = np.maximum(s, t - r + 1)
+    extra = ((gs[None, :] >= s) & (gs[None, :] < lo[:, None]) & (gs[None, :] <= t[:, None])).sum(axis=1)
+    n = n + extra
+    n[gs] = gs + 1
+    return int(n.sum())
+
+
+def bench_global(torch, swa, w, G, steps=10, settle=_no_settle):
+    """Prefill with task-bound global tokens at positions G on a prefill
+    workload's tensors: the banded pass, the merge of each row's global keys
+    and the dense global rows; algorithmic TFLOP/s of the key sets."""
+    q, k, v = __import__("swa_inputs").prefill_inputs(w)
+    qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
+    del q, k, v
+    out = torch.empty_like(qd)
+    desc = swa.make_desc(w.B, w.Hq, w.Hkv, w.d, w.s, w.r, torch.bfloat16)
+    ws = torch.empty(swa._lib.swa_prefill_global_workspace_bytes(desc, w.L, len(G)), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda: swa.prefill_global(qd, kd, vd, w.s, w.r, G, out=out, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    settle()
+    ms = time_launches(torch, call, steps)
+    flops = 4.0 * w.d * global_key_count_sum(w.L, w.s, w.r, G) * w.B * w.Hq
+    plain = prefill_flops(w)
+    return {"ms": ms, "tflops": flops / ms / 1e9, "globals": list(G), "flops": flops,
+            "extra_flops_over_window": flops - plain}
+
+
 def backward_flops(w) -> float:
     """Algorithmic flops of the backward: 10 d per (query, key) pair of the key
     set (the scores, dout . v, and the dq, dk and dv products, 2 d each)."""
@@ -492,7 +527,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="time only these legs (comma list: 5 = the main chunked step, 2, 3 = prefill "
-                         "workloads, 4 = decode, 9 = backward, 6, 7, 8, 1 = sweeps / dilated / fp32)")
+                         "workloads, 4 = decode, 9 = backward, 10 = global tokens, 6, 7, 8, 1 = sweeps / "
+                         "dilated / fp32)")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps (default: the workload's 1024)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
@@ -525,7 +561,7 @@ def main():
         print(json.dumps({"copy_calibration_bytes": src.numel() * 2, "dispatches": 3}))
         return
 
-    todo = {5, 2, 3, 4, 9, 6, 7, 8, 1} if args.only is None else {int(x) for x in args.only.split(",") if x}
+    todo = {5, 2, 3, 4, 9, 10, 6, 7, 8, 1} if args.only is None else {int(x) for x in args.only.split(",") if x}
     w2 = si.WORKLOADS[2]
     settle = Settler(torch, swa, w2, args.settle_ms) if args.settle_ms > 0 else _no_settle
     rooflines, extra = {}, {}
@@ -574,6 +610,13 @@ def main():
                 "frac": rb["tflops"] / PEAK_BF16_TFLOPS, "flops_per_call": rb["flops"], "call_ms": rb["ms"]}
             log("backward", wb.name, rb)
             torch.cuda.empty_cache()
+    if 10 in todo:
+        # task-bound global tokens on the 4+1020 workload's tensors
+        w3 = si.WORKLOADS[3]
+        extra["global_tokens_" + w3.name] = bench_global(torch, swa, w3, [2, 100, 2000, 2001, 7777, 12000, 12500,
+                                                                          16383], settle=settle)
+        log("global", extra["global_tokens_" + w3.name])
+        torch.cuda.empty_cache()
     if 6 in todo:
         # window sweep on the GQA workload's tensors, to the full-attention limit
         extra["window_sweep_" + w2.name] = bench_window_sweep(torch, swa, w2, [512, 1024, 2048, 4096, 8192],

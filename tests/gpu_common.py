@@ -47,3 +47,17 @@ def max_err(a, b) -> float:
     assert a.shape == b.shape, (a.shape, b.shape)
     assert np.isfinite(a).all(), "non-finite GPU output"
     return float(np.abs(a - b).max()) if a.size else 0.0
+
+
+def guarded(shape, dtype, fill, pad=4096):
+    """A device tensor of `shape` inside a buffer with `pad` canary elements
+    (value `fill`) before and after; returns (buffer, view)."""
+    n = 1
+    for x in shape:
+        n *= x
+    buf = torch.full((n + 2 * pad,), fill, dtype=dtype, device="cuda")
+    return buf, buf[pad:pad + n].view(*shape)
+
+
+def guard_intact(buf, fill, pad=4096) -> bool:
+    return bool((buf[:pad] == fill).all()) and bool((buf[-pad:] == fill).all())

@@ -93,3 +93,9 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_global_key_count_sum_is_the_sum_of_key_set_sizes():
+    for L, s, r, G in [(300, 4, 28, [2, 50, 51, 299]), (200, 0, 16, [0, 7, 100]), (90, 70, 10, [3, 80])]:
+        want = sum(len(oracle.key_set(t, s, r, globals_=G)) for t in range(L))
+        assert bench.global_key_count_sum(L, s, r, G) == want

@@ -296,3 +296,27 @@ def test_decode_rope_full_size_sampled(gpu):
     rows = np.array([[b, h, w.L + i] for i in range(nsteps) for b in range(len(pick)) for h in range(w.Hq)])
     ref = oracle.prefill_rows(Q, K, V, w.s, w.r, rope_base=base, rows=rows).reshape(nsteps, len(pick), w.Hq, w.d)
     assert max_err(got, ref) <= TOL["bf16"]
+
+
+def test_decode_full_attention_32k_sampled(gpu):
+    """Full attention over a 32768-token context on the decode workload's
+    shape (B = 64, GQA 32/8, d = 128): a cache of 4 + 32764 slots, every slot
+    valid, the size the bench's cache-size sweep times; every head of three
+    sequences against the fp64 decode row over all slots."""
+    import sliding_window_attention_sink_amd as swa
+    B, Hq, Hkv, d, s, r = 64, 32, 8, 128, 4, 32764
+    S = s + r
+    g = torch.Generator(device="cuda").manual_seed(21)
+    kc = torch.randn((B, Hkv, S, d), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((B, Hkv, S, d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    say("decode 32k full attention")
+    o = swa.decode(q, kc, vc, S + 100, s, r)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for b in (0, 31, B - 1):
+        kh, vh, qh = host(kc[b]), host(vc[b]), host(q[b])
+        got = host(o[b])
+        for h in range(Hq):
+            ref = oracle.attend_set(qh[h], kh[h // G], vh[h // G])
+            assert max_err(got[h], ref) <= TOL["bf16"], (b, h)

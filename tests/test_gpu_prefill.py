@@ -248,3 +248,40 @@ def test_stream_argument(gpu):
     side.synchronize()
     ref = oracle.prefill_rows(q, k, v, 4, 60).reshape(o.shape)
     assert max_err(host(o), ref) <= TOL["bf16"]
+
+
+def test_dominant_sinks_at_the_4_plus_1020_length(gpu):
+    """Sinks that take most of the softmax mass, at the StreamingLLM
+    workload's length and heads (one sequence of B = 4, H = 32, L = 16384,
+    4 + 1020): Q = N(0,1) + 3u and the four sink keys 30u for a unit vector
+    u per head, so sink scores sit near 8 against window scores near 0.
+    The realised sink mass (from fp64 scores on the sampled rows) is above
+    one half, and the sampled rows match the oracle."""
+    import sliding_window_attention_sink_amd as swa
+    w = si.WORKLOADS[3]
+    B, H, L, d, s, r = 1, w.Hq, w.L, w.d, w.s, w.r
+    g = np.random.default_rng(31)
+    u = g.standard_normal((B, H, 1, d))
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    q = si.round_bf16((g.standard_normal((B, H, L, d)) + 3.0 * u).astype(np.float32))
+    k = si.round_bf16(g.standard_normal((B, H, L, d)).astype(np.float32))
+    k[:, :, :s] = si.round_bf16(np.broadcast_to(30.0 * u, (B, H, s, d)).astype(np.float32))
+    v = si.round_bf16(g.standard_normal((B, H, L, d)).astype(np.float32))
+    say("dominant sinks 16384")
+    o = swa.prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), s, r)
+    torch.cuda.synchronize()
+    rows = np.array([[0, h, t] for h in range(0, H, 3) for t in list(range(0, L, 997)) + [L - 1]])
+    ref = oracle.prefill_rows(q, k, v, s, r, rows=rows)
+    got = rows_of(host(o), rows)
+    assert max_err(got, ref) <= TOL["bf16"]
+    # realised sink mass over the sampled rows past the first window
+    mass = []
+    for _, h, t in rows:
+        if t < s + r:
+            continue
+        keys = oracle.key_set(int(t), s, r)
+        x = (k[0, h, keys].astype(np.float64) @ q[0, h, t].astype(np.float64)) / np.sqrt(d)
+        p = np.exp(x - x.max())
+        mass.append(p[:s].sum() / p.sum())
+    print("realised sink mass: mean %.3f, min %.3f" % (np.mean(mass), np.min(mass)))
+    assert np.mean(mass) > 0.5
