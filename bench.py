@@ -286,7 +286,8 @@ def dilated_key_count_sum(L: int, s: int, r: int, dil: int) -> int:
 
 
 def bench_dilated(torch, swa, w, dilations, steps=10, settle=_no_settle):
-    """Dilated-window prefill of the GQA workload's tensors, algorithmic TFLOP/s."""
+    """Dilated-window prefill of a workload's tensors (read and written in
+    place, no workspace), algorithmic TFLOP/s."""
     q, k, v = __import__("swa_inputs").prefill_inputs(w)
     qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
     del q, k, v
@@ -295,16 +296,13 @@ def bench_dilated(torch, swa, w, dilations, steps=10, settle=_no_settle):
     res = {}
     settle()
     for dil in dilations:
-        ws = torch.empty(max(16, swa._lib.swa_prefill_dilated_workspace_bytes(desc, w.L, dil)), dtype=torch.uint8,
-                         device="cuda")
+        assert swa._lib.swa_prefill_dilated_workspace_bytes(desc, w.L, dil) == 0
         for _ in range(2):
-            swa.prefill_dilated(qd, kd, vd, w.s, w.r, dil, out=out, workspace=ws)
+            swa.prefill_dilated(qd, kd, vd, w.s, w.r, dil, out=out)
         torch.cuda.synchronize()
-        ms = time_launches(torch, lambda: swa.prefill_dilated(qd, kd, vd, w.s, w.r, dil, out=out, workspace=ws),
-                           steps)
+        ms = time_launches(torch, lambda: swa.prefill_dilated(qd, kd, vd, w.s, w.r, dil, out=out), steps)
         flops = 4.0 * w.d * dilated_key_count_sum(w.L, w.s, w.r, dil) * w.B * w.Hq
         res["dilation%d" % dil] = {"ms": ms, "tflops": flops / ms / 1e9, "reach": w.s + dil * (w.r - 1) + 1}
-        del ws
     return res
 
 
@@ -624,6 +622,8 @@ def main():
         torch.cuda.empty_cache()
     if 7 in todo:
         extra["dilated_" + w2.name] = bench_dilated(torch, swa, w2, [2, 4], settle=settle)
+        w3 = si.WORKLOADS[3]
+        extra["dilated_" + w3.name] = bench_dilated(torch, swa, w3, [2, 8], settle=settle)
         torch.cuda.empty_cache()
     if 8 in todo:
         w4 = si.WORKLOADS[4]

@@ -133,12 +133,13 @@ int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new,
  * the Longformer section of the t6page page "滑窗与固定稀疏": attended
  * positions skip dilation-1 tokens, the number of keys is unchanged).
  * Layouts as for swa_prefill.  dilation = 1 is swa_prefill without a cache.
- * Otherwise the positions of each residue class mod dilation (after the
- * sink rows) are gathered into a workspace of
- * swa_prefill_dilated_workspace_bytes() bytes, attended as an ordinary
- * window and scattered back.  Errors: those of swa_prefill, and
- * SWA_ERR_INVALID_ARG for dilation < 1 or a short/NULL workspace,
- * SWA_ERR_UNSUPPORTED with RoPE.
+ * Otherwise the rows of each residue class mod dilation from position s on
+ * form an ordinary window over the sinks; they are read and written in
+ * place (row stride dilation * d), every class in one launch, after one
+ * launch for the s sink rows.  No workspace: workspace may be NULL, and
+ * swa_prefill_dilated_workspace_bytes() returns 0 (kept for callers that
+ * size one).  Errors: those of swa_prefill, SWA_ERR_INVALID_ARG for
+ * dilation < 1 or > 65536, SWA_ERR_UNSUPPORTED with RoPE.
  */
 size_t swa_prefill_dilated_workspace_bytes(const swa_desc* desc, int64_t L, int32_t dilation);
 int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, const void* k, const void* v, void* o,

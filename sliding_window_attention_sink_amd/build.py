@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libswa.so")
 
-SOURCES = ["swa_api.cpp", "prefill.hip", "prefill_bf16.hip", "decode.hip", "append.hip", "rope.hip", "dilate.hip",
+SOURCES = ["swa_api.cpp", "prefill.hip", "prefill_bf16.hip", "decode.hip", "append.hip", "rope.hip",
            "backward.hip", "global.hip"]
 ARCH = "gfx950"
 

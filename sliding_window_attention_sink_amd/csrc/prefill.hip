@@ -72,12 +72,14 @@ struct Tiles<float, D> {
         }
     }
 
-    static __device__ __forceinline__ void load_contig(Regs& R, const float* kb, const float* vb, int tid) {
-        const int ofs = (tid / CH) * D + (tid % CH) * 4;
+    // rows rs elements apart
+    static __device__ __forceinline__ void load_contig(Regs& R, const float* kb, const float* vb, int64_t rs,
+                                                       int tid) {
+        const int64_t ofs = (tid / CH) * rs + (tid % CH) * 4;
 #pragma unroll
         for (int ld = 0; ld < LD; ++ld) {
-            R.k[ld] = *(const u32x4*)(kb + ofs + ld * (NT / CH) * D);
-            R.v[ld] = *(const u32x4*)(vb + ofs + ld * (NT / CH) * D);
+            R.k[ld] = *(const u32x4*)(kb + ofs + ld * (NT / CH) * rs);
+            R.v[ld] = *(const u32x4*)(vb + ofs + ld * (NT / CH) * rs);
         }
     }
 
@@ -151,7 +153,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
     const int w = xcd_work_item(blockIdx.x, gridDim.x);
     const int mt = a.n_mtiles - 1 - (w % a.n_mtiles);   // late (heavier) query tiles first
     const int bh = w / a.n_mtiles;
-    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int h = bh % a.Hq;
+    int b = bh / a.Hq;
     const int kvh = h / (a.Hq / a.Hkv);
     const int s = a.s, r = a.r;
     const int pos0 = (int)a.pos0;
@@ -160,8 +163,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: keep it scalar
     const int l32 = lane & 31, g = lane >> 5;
 
+    // residue classes: batch index b dil + c, own rows first(c) + i dil
+    int64_t Lown = a.L, own_off = 0;
+    if (a.dil > 1) {
+        const int c = b % a.dil;
+        b /= a.dil;
+        const int64_t first = pos0 + ((c - pos0) % a.dil + a.dil) % a.dil;
+        Lown = first < a.Lp ? (a.Lp - 1 - first) / a.dil + 1 : 0;
+        own_off = first * D;
+    }
     const int row0 = mt * BM;                                   // first row of the tile (call-relative)
-    const int nrows = (int)((a.L - row0) < BM ? (a.L - row0) : BM);
+    if (row0 >= Lown) return;                                   // a shorter class's last tile
+    const int nrows = (int)((Lown - row0) < BM ? (Lown - row0) : BM);
     const int t0 = pos0 + row0, t1 = t0 + nrows - 1;            // positions of the tile's rows
     const int tw0 = t0 + wave * WROWS;
     const int tw1 = (tw0 + WROWS - 1) < t1 ? (tw0 + WROWS - 1) : t1;
@@ -169,19 +182,20 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
     const int my_t = tw0 + l32;
     const bool my_valid = my_t <= t1;
 
-    const size_t qoff = ((size_t)bh * a.L + row0 + wave * WROWS + l32) * D;
-    const T* kn = (const T*)a.kn + (size_t)(b * a.Hkv + kvh) * a.L * D;
-    const T* vn = (const T*)a.vn + (size_t)(b * a.Hkv + kvh) * a.L * D;
-    const T* kc = a.kc ? (const T*)a.kc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
-    const T* vc = a.vc ? (const T*)a.vc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
+    const int64_t rs = a.rs;
+    const size_t qoff = (size_t)(b * a.Hq + h) * a.q_bh + own_off + (size_t)(row0 + wave * WROWS + l32) * rs;
+    const T* kn = (const T*)a.kn + (size_t)(b * a.Hkv + kvh) * a.kv_bh + own_off;
+    const T* vn = (const T*)a.vn + (size_t)(b * a.Hkv + kvh) * a.kv_bh + own_off;
+    const T* kc = a.kc ? (const T*)a.kc + (size_t)(b * a.Hkv + kvh) * a.c_bh : nullptr;
+    const T* vc = a.vc ? (const T*)a.vc + (size_t)(b * a.Hkv + kvh) * a.c_bh : nullptr;
 
     auto kptr = [&](int p) __attribute__((always_inline)) -> const T* {
-        if (p >= pos0) return kn + (size_t)(p - pos0) * D;
+        if (p >= pos0) return kn + (size_t)(p - pos0) * rs;
         int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
         return kc + (size_t)sl * D;
     };
     auto vptr = [&](int p) __attribute__((always_inline)) -> const T* {
-        if (p >= pos0) return vn + (size_t)(p - pos0) * D;
+        if (p >= pos0) return vn + (size_t)(p - pos0) * rs;
         int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
         return vc + (size_t)sl * D;
     };
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(PrefillArgs a) {
             const int kbase = j * BN, klast = kbase + BN - 1;
             const bool all_needed = klast <= t1 && (kbase >= lo_any || klast < P.sink_hi);
             if (all_needed && kbase >= pos0) {
-                TL::load_contig(regs, kn + (size_t)(kbase - pos0) * D, vn + (size_t)(kbase - pos0) * D, tid);
+                TL::load_contig(regs, kn + (size_t)(kbase - pos0) * rs, vn + (size_t)(kbase - pos0) * rs, rs, tid);
             } else if (all_needed && kbase >= s && klast < pos0) {
                 TL::load_ring(regs, kc, vc, s + kbase % r, s + r, r, tid);
             } else {

@@ -245,8 +245,8 @@ struct PP {
     // O^T accumulator layout straight to HBM cost several microseconds per
     // workgroup).  Rows from nvalid on are not stored.
     static constexpr int ORS = RB + 16;
-    static __device__ __forceinline__ void store_o(char* lds, __bf16* orow0, const f32x16* o, float inv, int lane,
-                                                   int nvalid) {
+    static __device__ __forceinline__ void store_o(char* lds, __bf16* orow0, uint32_t orsb, const f32x16* o,
+                                                   float inv, int lane, int nvalid) {
         const int row = lane & 31, g = lane >> 5;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -271,7 +271,7 @@ struct PP {
         for (int i = 0; i < WROWS / RPI; ++i) {
             const int r = RPI * i + rr;
             const u32x4 x = *(const u32x4*)(lds + r * ORS + 16 * cc);
-            if (r < nvalid) *(u32x4*)((char*)orow0 + (size_t)r * RB + 16 * cc) = x;
+            if (r < nvalid) *(u32x4*)((char*)orow0 + (size_t)r * orsb + 16 * cc) = x;
         }
     }
 };
@@ -350,7 +350,19 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         tok = 256;
         row0 = mt * tok;
     }
-    const int nrows = (int)((a.L - row0) < tok ? (a.L - row0) : tok);
+    // Residue classes: the item's batch index is b * dil + c, and the own
+    // rows of class c are the positions first(c), first(c) + dil, ... below
+    // Lp (first(c) the first position >= pos0 in the class).
+    int64_t Lown = a.L, own_off = 0;
+    if (a.dil > 1) {
+        const int c = b % a.dil;
+        b /= a.dil;
+        const int64_t first = pos0 + ((c - pos0) % a.dil + a.dil) % a.dil;
+        Lown = first < a.Lp ? (a.Lp - 1 - first) / a.dil + 1 : 0;
+        own_off = first * D;
+    }
+    if (row0 >= Lown) return;   // a shorter class's last tile (workgroup-uniform, before any barrier)
+    const int nrows = (int)((Lown - row0) < tok ? (Lown - row0) : tok);
     const int t0 = pos0 + row0, t1 = t0 + nrows - 1;                  // the workgroup's rows
     const int wrow0 = row0 + (a.pair_mode ? 0 : 128 * grp) + WROWS * sub;   // this wave's first row (call-relative)
     const int tw0 = pos0 + wrow0;
@@ -359,11 +371,12 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     const int my_t = tw0 + l32;
     const bool my_valid = my_t <= t1;
 
-    const size_t qoff = ((size_t)(b * a.Hq + h) * a.L + wrow0 + l32) * D;
-    const __bf16* kn = (const __bf16*)a.kn + (size_t)(b * a.Hkv + kvh) * a.L * D;
-    const __bf16* vn = (const __bf16*)a.vn + (size_t)(b * a.Hkv + kvh) * a.L * D;
-    const __bf16* kc = a.kc ? (const __bf16*)a.kc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
-    const __bf16* vc = a.vc ? (const __bf16*)a.vc + (size_t)(b * a.Hkv + kvh) * (s + r) * D : nullptr;
+    const int64_t rs = a.rs;                                           // elements between own rows
+    const size_t qoff = (size_t)(b * a.Hq + h) * a.q_bh + own_off + (size_t)(wrow0 + l32) * rs;
+    const __bf16* kn = (const __bf16*)a.kn + (size_t)(b * a.Hkv + kvh) * a.kv_bh + own_off;
+    const __bf16* vn = (const __bf16*)a.vn + (size_t)(b * a.Hkv + kvh) * a.kv_bh + own_off;
+    const __bf16* kc = a.kc ? (const __bf16*)a.kc + (size_t)(b * a.Hkv + kvh) * a.c_bh : nullptr;
+    const __bf16* vc = a.vc ? (const __bf16*)a.vc + (size_t)(b * a.Hkv + kvh) * a.c_bh : nullptr;
 
     // ---- tiles of the workgroup: phase 0 then phase 1, as one list
     Phase ph0 = {0, -1, 0, NO_BAND, 0}, ph1 = {0, -1, 0, NO_BAND, 0};
@@ -407,7 +420,10 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // Past the last tile the last tile is read again into the given set (a
     // buffer region no later cluster reads), so every wave always issues
     // the same number of loads.
-    const uint32_t kloff = (uint32_t)(kkey0 * T::RB + kchk), vloff = (uint32_t)(vkey0 * T::RB + vchk);
+    // (own rows are rsb bytes apart; a tile of own rows spans 64 rsb bytes,
+    // which the host keeps below 2^31)
+    const uint32_t rsb = (uint32_t)(2 * rs);
+    const uint32_t kloff = (uint32_t)kkey0 * rsb + (uint32_t)kchk, vloff = (uint32_t)vkey0 * rsb + (uint32_t)vchk;
     auto issue = [&](auto is_k_c, int v, int set) __attribute__((always_inline)) {
         constexpr bool is_k = decltype(is_k_c)::value;
         u32x4* dst0 = is_k ? smem[set].k : smem[set].v;
@@ -422,10 +438,10 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         const int chk = is_k ? kchk : vchk;
         if (all_needed && kbase >= pos0) {
             // the call's own rows kbase.. (contiguous)
-            const __bf16* base = own + (size_t)(kbase - pos0) * D;
+            const __bf16* base = own + (size_t)(kbase - pos0) * rs;
 #pragma unroll
             for (int j = 0; j < T::JN; ++j)
-                load_lds16_off(base + (size_t)T::JSTEP * j * D, is_k ? kloff : vloff, dst0 + 64 * (sub + GW * j));
+                load_lds16_off(base + (size_t)T::JSTEP * j * rs, is_k ? kloff : vloff, dst0 + 64 * (sub + GW * j));
         } else if (all_needed && kbase >= s && klast < pos0) {
             // rolling cache slots s + (p mod r), at most one wrap in a tile
             const __bf16* base = cache + (size_t)s * D;
@@ -449,7 +465,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
                 p = p < t1 ? p : t1;
                 const __bf16* rowp;
                 if (p >= pos0) {
-                    rowp = own + (size_t)(p - pos0) * D;
+                    rowp = own + (size_t)(p - pos0) * rs;
                 } else {
                     const int sl = p < s ? p : s + (int)((unsigned)p % (unsigned)r);
                     rowp = cache + (size_t)sl * D;
@@ -507,13 +523,16 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         vc_hi = vc_hi < nv - 1 ? vc_hi : nv - 1;
         if (vc_lo <= vc_hi) relc0 = (BN * (vo0 + vc_lo)) % r;
     }
-    // issue() with the contiguous runs taken by a pointer step
+    // issue() with the contiguous runs taken by a pointer step.  The cache
+    // runs share the own rows' lane offsets: a call with a cache run (keys
+    // in [s, pos0)) has rs = d.  Residue classes set pos0 <= s, which leaves
+    // [vc_lo, vc_hi] empty.
     auto issue_run = [&](auto is_k_c, int v, int set) __attribute__((always_inline)) {
         constexpr bool is_k = decltype(is_k_c)::value;
         const int vv = v < nv ? v : nv - 1;
         const __bf16* base = nullptr;
         if (vv >= vf_lo && vv <= vf_hi) {
-            base = (is_k ? kn : vn) + (size_t)(BN * (vo0 + vv) - pos0) * D;
+            base = (is_k ? kn : vn) + (size_t)(BN * (vo0 + vv) - pos0) * rs;
         } else if (vv >= vc_lo && vv <= vc_hi) {
             int rel = relc0 + BN * (vv - vc_lo);
             rel = rel >= r ? rel - r : rel;
@@ -524,7 +543,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
             const uint32_t off = is_k ? kloff : vloff;
 #pragma unroll
             for (int j = 0; j < T::JN; ++j)
-                load_lds16_off(base, off + (uint32_t)(T::JSTEP * T::RB * j), dst0 + 64 * (sub + GW * j));
+                load_lds16_off(base, off + (uint32_t)(T::JSTEP * j) * rsb, dst0 + 64 * (sub + GW * j));
         } else {
             issue(is_k_c, v, set);
         }
@@ -780,9 +799,10 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     if (!wave_active) return;
     const float l_tot = l_part + __shfl_xor(l_part, 32);
     static_assert(PW * WROWS * T::ORS <= (int)sizeof(smem), "output staging fits the tile buffers");
-    T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * D, oacc,
+    T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * rs, rsb, oacc,
                my_valid ? 1.0f / l_tot : 0.0f, lane, tw1 - tw0 + 1);
-    if (a.lse != nullptr && my_valid && g == 0) a.lse[qoff / D] = m_c + __builtin_amdgcn_logf(l_tot);
+    if (a.lse != nullptr && my_valid && g == 0)
+        a.lse[(size_t)(b * a.Hq + h) * a.L + wrow0 + l32] = m_c + __builtin_amdgcn_logf(l_tot);
 }
 
 template <int D>

@@ -32,6 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int64_t kMaxPos = (int64_t)1 << 30;    // positions and slot counts stay in int32 arithmetic
+constexpr int32_t kMaxDilation = 65536;         // a 64-row tile of one residue class spans < 2^31 bytes
 
 // Shared descriptor checks; `need_bf16` for entry points built for bf16 only.
 int check_desc(const swa_desc* d, const char* fn) {
@@ -85,29 +86,6 @@ int32_t default_splits(const swa_desc* d) {
     if (n > 64) n = 64;
     if (n < 1) n = 1;
     return (int32_t)n;
-}
-
-// Residue-class layout of a dilated prefill: every class sequence holds the
-// s1 = min(s, L) sink rows and then its positions >= s1 (at most
-// ceil((L - s1) / dil) of them); Q, K, V and O copies of that shape.
-struct DilateLayout {
-    int64_t s1 = 0, Lc = 0;
-    size_t q = 0, k = 0, v = 0, o = 0, total = 0;
-};
-
-DilateLayout dilate_layout(const swa_desc* d, int64_t L, int64_t dil) {
-    DilateLayout x;
-    x.s1 = d->s < L ? d->s : L;
-    x.Lc = x.s1 + (L - x.s1 + dil - 1) / dil;
-    const size_t rb = (size_t)d->d * elem_bytes(d);
-    const size_t qn = round_up((size_t)d->B * dil * d->Hq * x.Lc * rb, 256);
-    const size_t kn = round_up((size_t)d->B * dil * d->Hkv * x.Lc * rb, 256);
-    x.q = 0;
-    x.k = qn;
-    x.v = qn + kn;
-    x.o = qn + 2 * kn;
-    x.total = 2 * qn + 2 * kn;
-    return x;
 }
 
 // Backward workspace: per-row log-sum-exp and D (each padded by a query
@@ -164,6 +142,48 @@ size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L) {
 namespace {
 
 // swa_prefill; lse (null or [B, Hq, L]) receives each row's log2-sum-exp.
+// Query tiles per (batch, q-head) for L rows
+int64_t prefill_mtiles(const swa_desc* desc, int64_t L) {
+    const int64_t rows_per_block = desc->dtype == SWA_BF16 ? swa::prefill_bf16_rows_per_block(desc->Hq, desc->Hkv)
+                                                           : swa::kPrefillF32RowsPerBlock;
+    return (L + rows_per_block - 1) / rows_per_block;
+}
+
+// Kernel arguments of a call on dense [B, H, L, d] tensors (and a cache of
+// s + r slots per (batch, kv-head), or none)
+swa::PrefillArgs dense_prefill_args(const swa_desc* desc, const void* q, const void* k, const void* v, void* o,
+                                    int64_t L, const void* k_cache, const void* v_cache, int64_t pos0) {
+    swa::PrefillArgs a{};
+    a.q = q;
+    a.kn = k;
+    a.vn = v;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.o = o;
+    a.L = L;
+    a.pos0 = pos0;
+    a.rs = desc->d;
+    a.q_bh = L * desc->d;
+    a.kv_bh = L * desc->d;
+    a.c_bh = ((int64_t)desc->s + desc->r) * desc->d;
+    a.dil = 1;
+    a.Lp = L;
+    a.B = desc->B;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.s = desc->s;
+    a.r = desc->r;
+    a.n_mtiles = (int32_t)prefill_mtiles(desc, L);
+    a.merge_sink = 1;
+    a.pair_mode = (desc->dtype == SWA_BF16 && (desc->Hq / desc->Hkv) % 2 == 0) ? 1 : 0;
+    a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
+    return a;
+}
+
+hipError_t launch_prefill(const swa_desc* desc, const swa::PrefillArgs& a, hipStream_t hs) {
+    return desc->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, desc->d, hs) : swa::launch_prefill_f32(a, desc->d, hs);
+}
+
 int prefill_impl(const char* fn, const swa_desc* desc, const void* q, const void* k, const void* v, void* o,
                  int64_t L, const void* k_cache, const void* v_cache, int64_t pos0, float* lse, void* stream) {
     clear_error();
@@ -182,41 +202,18 @@ int prefill_impl(const char* fn, const swa_desc* desc, const void* q, const void
         return fail(SWA_ERR_INVALID_ARG, "%s: pos0 > 0 needs the rolling cache", fn);
     }
     const bool rope = desc->rope_base > 0.0f;
-    const bool bf16 = desc->dtype == SWA_BF16;
-    const int64_t rows_per_block =
-        bf16 ? swa::prefill_bf16_rows_per_block(desc->Hq, desc->Hkv) : swa::kPrefillF32RowsPerBlock;
-    const int64_t mtiles = (L + rows_per_block - 1) / rows_per_block;
-    if ((int64_t)desc->B * desc->Hq * mtiles > 0x7fffffffLL)
+    if ((int64_t)desc->B * desc->Hq * prefill_mtiles(desc, L) > 0x7fffffffLL)
         return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
 
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    swa::PrefillArgs a{};
-    a.q = q;
-    a.kn = k;
-    a.vn = v;
-    a.kc = has_cache ? k_cache : nullptr;
-    a.vc = has_cache ? v_cache : nullptr;
-    a.o = o;
-    a.L = L;
-    a.pos0 = pos0;
-    a.B = desc->B;
-    a.Hq = desc->Hq;
-    a.Hkv = desc->Hkv;
-    a.s = desc->s;
-    a.r = desc->r;
-    a.n_mtiles = (int32_t)mtiles;
-    a.merge_sink = 1;
-    a.pair_mode = (bf16 && (desc->Hq / desc->Hkv) % 2 == 0) ? 1 : 0;
-    a.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
-
+    swa::PrefillArgs a = dense_prefill_args(desc, q, k, v, o, L, has_cache ? k_cache : nullptr,
+                                            has_cache ? v_cache : nullptr, pos0);
     if (rope) {
         // the keys (own and cached) come rotated; the kernel turns the queries
         a.merge_sink = 0;
         a.rope_rr = rope_rr(desc);
     }
     a.lse = lse;
-    hipError_t e = bf16 ? swa::launch_prefill_bf16(a, desc->d, hs) : swa::launch_prefill_f32(a, desc->d, hs);
-    return hip_status(e, fn);
+    return hip_status(launch_prefill(desc, a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 }  // namespace
@@ -411,50 +408,55 @@ int swa_prefill_global(const swa_desc* desc, const void* q, const void* k, const
 }
 
 size_t swa_prefill_dilated_workspace_bytes(const swa_desc* desc, int64_t L, int32_t dilation) {
-    if (check_desc(desc, "swa_prefill_dilated_workspace_bytes") != SWA_OK || L < 1 || dilation < 1) return 0;
-    if (dilation == 1 || desc->rope_base > 0.0f) return 0;
-    return dilate_layout(desc, L, dilation).total;
+    (void)desc;
+    (void)L;
+    (void)dilation;
+    return 0;
 }
 
 int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, const void* k, const void* v, void* o,
                         int64_t L, void* workspace, size_t workspace_bytes, void* stream) {
     static const char* fn = "swa_prefill_dilated";
+    (void)workspace;
+    (void)workspace_bytes;
     clear_error();
     int st = check_desc(desc, fn);
     if (st) return st;
     if (dilation < 1) return fail(SWA_ERR_INVALID_ARG, "%s: dilation must be >= 1 (got %d)", fn, dilation);
+    if (dilation > kMaxDilation)
+        return fail(SWA_ERR_INVALID_ARG, "%s: dilation must be <= %d (got %d)", fn, kMaxDilation, dilation);
     if (desc->rope_base > 0.0f) return fail(SWA_ERR_UNSUPPORTED, "%s: dilation with RoPE is not built", fn);
-    if (dilation == 1) return swa_prefill(desc, q, k, v, o, L, nullptr, nullptr, 0, workspace, workspace_bytes, stream);
+    // with L <= s every row is a sink row (keys 0 .. t), the plain window's rows
+    if (dilation == 1 || L <= desc->s)
+        return prefill_impl(fn, desc, q, k, v, o, L, nullptr, nullptr, 0, nullptr, stream);
     if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k, fn, "k")) || (st = check_ptr(v, fn, "v")) ||
-        (st = check_ptr(o, fn, "o")) || (st = check_ptr(workspace, fn, "workspace")))
+        (st = check_ptr(o, fn, "o")))
         return st;
-    if (L < 1) return fail(SWA_ERR_INVALID_ARG, "%s: L must be >= 1 (got %lld)", fn, (long long)L);
     if (L > kMaxPos) return fail(SWA_ERR_INVALID_ARG, "%s: positions beyond 2^30", fn);
-    if ((int64_t)desc->B * dilation > 0x7fffffffLL) return fail(SWA_ERR_INVALID_ARG, "%s: B * dilation too large", fn);
-    const DilateLayout lay = dilate_layout(desc, L, dilation);
-    if (workspace_bytes < lay.total)
-        return fail(SWA_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
-
+    const int64_t s = desc->s, d = desc->d;
+    const int64_t n_max = (L - s + dilation - 1) / dilation;   // rows of the longest class
+    if ((int64_t)desc->B * dilation * desc->Hq * prefill_mtiles(desc, n_max) > 0x7fffffffLL)
+        return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
-    swa::DilateArgs da{};
-    da.L = L;
-    da.Lc = lay.Lc;
-    da.s1 = lay.s1;
-    da.dil = dilation;
-    da.B = desc->B;
-    da.row_bytes = (int32_t)(desc->d * elem_bytes(desc));
-    if ((st = hip_status(swa::launch_dilate_gather(da, q, ws + lay.q, desc->Hq, hs), fn)) ||
-        (st = hip_status(swa::launch_dilate_gather(da, k, ws + lay.k, desc->Hkv, hs), fn)) ||
-        (st = hip_status(swa::launch_dilate_gather(da, v, ws + lay.v, desc->Hkv, hs), fn)))
-        return st;
-    // the classes are extra batch entries of an ordinary prefill
-    swa_desc cd = *desc;
-    cd.B = (int32_t)(desc->B * dilation);
-    if ((st = swa_prefill(&cd, ws + lay.q, ws + lay.k, ws + lay.v, ws + lay.o, lay.Lc, nullptr, nullptr, 0, nullptr,
-                          0, stream)))
-        return st;
-    return hip_status(swa::launch_dilate_scatter(da, ws + lay.o, o, desc->Hq, hs), fn);
+
+    // 1. the sink rows 0 .. s-1 (keys 0 .. t): the plain window on the first
+    //    s rows of each (batch, head)
+    if (s > 0) {
+        swa::PrefillArgs a = dense_prefill_args(desc, q, k, v, o, s, nullptr, nullptr, 0);
+        a.q_bh = a.kv_bh = L * d;
+        if ((st = hip_status(launch_prefill(desc, a, hs), fn))) return st;
+    }
+    // 2. every residue class mod dilation in one launch, read and written in
+    //    place: class c's rows p >= s, p = c (mod dilation), are the own rows
+    //    of a call at pos0 = s with row stride dilation * d, and its sinks are
+    //    the cache slots 0 .. s-1, i.e. the first s rows of K and V
+    swa::PrefillArgs a = dense_prefill_args(desc, q, k, v, o, n_max, s > 0 ? k : nullptr, s > 0 ? v : nullptr, s);
+    a.rs = (int64_t)dilation * d;
+    a.q_bh = a.kv_bh = a.c_bh = L * d;
+    a.dil = dilation;
+    a.Lp = L;
+    a.B = (int32_t)(desc->B * dilation);
+    return hip_status(launch_prefill(desc, a, hs), fn);
 }
 
 int32_t swa_decode_default_splits(const swa_desc* desc) {

@@ -21,8 +21,20 @@ struct PrefillArgs {
     const void* kc;
     const void* vc;
     void* o;
-    int64_t L;
+    int64_t L;          // own rows per (b, head); with dil > 1 see Lp
     int64_t pos0;
+    // Element strides: own row i of (b, head) sits at (b H + head) q_bh +
+    // i rs in q and o, and at (b Hkv + kvh) kv_bh + i rs in kn and vn;
+    // cache slot j at (b Hkv + kvh) c_bh + j d.  Dense calls: rs = d,
+    // q_bh = kv_bh = L d, c_bh = (s + r) d.
+    int64_t rs, q_bh, kv_bh, c_bh;
+    // Residue classes (dil > 1; with pos0 <= s and rs = dil d): the grid's
+    // batch index is b dil + c, and the own rows of class c are the
+    // positions first(c), first(c) + dil, ... below Lp, with first(c) the
+    // first position >= pos0 that is c mod dil (row i at element offset
+    // first(c) d + i rs).  Cache slots 0 .. pos0-1 hold the sinks.
+    int32_t dil;
+    int64_t Lp;
     int32_t B, Hq, Hkv, s, r;
     int32_t n_mtiles;   // query tiles per (b, q-head)
     int32_t merge_sink; // 1: sinks may share tiles with the band (same queries for both)
@@ -101,16 +113,6 @@ int prefill_bf16_rows_per_block(int Hq, int Hkv);
 // Launchers (return hipError_t of the launch).  `d` selects the instantiation.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, hipStream_t st);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t st);
-// Dilated window: residue-class sequences [B * dil, H, Lc, row_bytes] <->
-// positions [B, H, L, row_bytes]; s1 = min(s, L) sink rows lead every class.
-struct DilateArgs {
-    int64_t L, Lc, s1, dil;
-    int32_t B;
-    int32_t row_bytes;   // d * element size, a multiple of 16
-};
-
-hipError_t launch_dilate_gather(const DilateArgs& a, const void* src, void* dst, int32_t H, hipStream_t st);
-hipError_t launch_dilate_scatter(const DilateArgs& a, const void* src, void* dst, int32_t H, hipStream_t st);
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, int d, hipStream_t st);
 

@@ -156,18 +156,19 @@ def test_decode_step_rejects():
 
 def test_prefill_dilated_rejects():
     d_ = desc()
-    wsb = _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 3)
-    assert wsb > 0 and _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 1) == 0
-    assert _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 0) == 0
+    # the classes are read and written in place: no workspace at any dilation
+    assert _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 3) == 0
+    assert _lib.swa_prefill_dilated_workspace_bytes(d_, 100, 1) == 0
 
-    def dil(dd=d_, dl=3, ws=W, n=wsb, L=100):
-        return _lib.swa_prefill_dilated(dd, dl, A, B_, C, D, L, ws, n, None)
+    def dil(dd=d_, dl=3, L=100):
+        return _lib.swa_prefill_dilated(dd, dl, A, B_, C, D, L, None, 0, None)
 
     assert dil(dl=0) == -1 and "dilation" in _lib.swa_last_error()
+    assert dil(dl=65537) == -1 and "dilation" in _lib.swa_last_error()
     assert dil(dd=desc(rope_base=1e4)) == -2
-    assert dil(ws=None) == -1 and "workspace" in _lib.swa_last_error()
-    assert dil(n=wsb - 16) == -1 and "workspace" in _lib.swa_last_error()
     assert dil(L=0) == -1
+    assert _lib.swa_prefill_dilated(d_, 3, None, B_, C, D, 100, None, 0, None) == -1
+    assert "q" in _lib.swa_last_error()
 
 
 def test_backward_rejects():

@@ -176,6 +176,10 @@ DILATED = [
     (62, "bf16", 1, 2, 1, 128, 500, 70, 20, 7),
     (63, "f32", 1, 2, 2, 64, 257, 4, 28, 4),
     (64, "bf16", 1, 2, 2, 128, 90, 4, 8, 100),
+    (66, "bf16", 2, 8, 2, 128, 3, 4, 16, 2),        # L < s: every row a sink row
+    (67, "bf16", 1, 4, 4, 64, 5, 4, 16, 3),         # L = s + 1: one class row
+    (68, "f32", 1, 4, 2, 128, 611, 2, 33, 5),
+    (69, "bf16", 1, 4, 2, 128, 1500, 1, 64, 2),     # several query tiles per class, ragged tail
 ]
 
 
@@ -201,6 +205,21 @@ def test_dilated_main_workload_sampled_rows(gpu):
     o = host(swa.prefill_dilated(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), w.s, w.r, 4))
     rows = sample_rows(w.B, w.Hq, w.L, 200, 31)
     ref = oracle.prefill_rows(q, k, v, w.s, w.r, rows=rows, dilation=4)
+    got = np.stack([o[b, h, t] for b, h, t in rows])
+    assert max_err(got, ref) <= TOL["bf16"]
+
+
+def test_dilated_4_plus_1020_sampled_rows(gpu):
+    """Dilation 8 at the 4+1020 workload's full size (B = 4, H = 32,
+    L = 16384): query tiles of 256 rows, classes of 2048 and 2047 rows
+    after the 4 sinks, a reach of 8188 positions."""
+    import sliding_window_attention_sink_amd as swa
+    w = si.WORKLOADS[3]
+    q, k, v = si.prefill_inputs(w)
+    say("dilated 4+1020 workload")
+    o = host(swa.prefill_dilated(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), w.s, w.r, 8))
+    rows = sample_rows(w.B, w.Hq, w.L, 160, 37)
+    ref = oracle.prefill_rows(q, k, v, w.s, w.r, rows=rows, dilation=8)
     got = np.stack([o[b, h, t] for b, h, t in rows])
     assert max_err(got, ref) <= TOL["bf16"]
 
