@@ -211,23 +211,53 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BackwardArgs a) {
 // dK and dV.  Work items: (b * Hkv + kvh, key tile of 128 keys, segment);
 // first the tiles holding sink keys (their queries run to the end), then
 // the others.  Segment seg of a tile walks its query blocks
-// [qb_lo + seg * segb, ...) for every q-head of the kv-head.
+// [qb_lo + seg * segb, ...) for every q-head of the kv-head: iteration it
+// is block qb_lo + seg * segb + it / G of q-head kvh * G + it % G.
+//
+// Eight waves in two groups of four share the tile's K and V in LDS; wave
+// (grp, sub) owns keys i0 + 32 sub .. +31 and the iterations it = grp (mod
+// 2), and the two groups alternate on each compute unit's SIMDs (a
+// ping-pong, one barrier per half-slot).  In half-slot h the group with
+// h = grp (mod 2) runs C: dV^T += dO^T P and dK^T += Q^T dS of iteration
+// h-2 and S = Q K^T, dP = dO V^T of iteration h (32 MFMAs); the other runs
+// X: the loads of iteration h+2 and the softmax of iteration h-1 (P from
+// the row's log-sum-exp, dS = P (dP - D), packed to bf16).  An iteration's
+// Q, dO and statistics stay in one of PB buffers from its loads (half-slot
+// it-2) to its transposed reads (half-slot it+2); a wave waits for its own
+// loads at the end of its next C half-slot, one barrier before their first
+// reader.  At the end group 1 hands its partial sums to group 0 through
+// LDS.
+constexpr int PB = 5;
+
 template <int D>
-__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid gr) {
+__global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid gr) {
     typedef Tile<D> TT;
     constexpr int KS = TT::KS, NDB = TT::NDB;
-    __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TT::BYTES];
-    __shared__ __attribute__((aligned(1024))) char kvs[2][NW][TT::BYTES];   // the tile's K and V, 32 keys a wave
-    __shared__ __attribute__((aligned(16))) float stat[NBUF][2][BLK];   // lse (log2 units), D
+    constexpr int TB = TT::BYTES;
+    constexpr int OFF_BUF = 2 * NW * TB;                 // after K and V of the tile
+    constexpr int OFF_STAT = OFF_BUF + PB * 2 * TB;
+    constexpr int LDS_BYTES = OFF_STAT + PB * 2 * BLK * 4;
+    // the final hand-over: 4 waves x (dK, dV) x NDB x 16 values x 64 lanes
+    static_assert(4 * 2 * NDB * 16 * 64 * 4 <= OFF_STAT, "hand-over fits the tile buffers");
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+    auto kv_tile = [&](int kv, int w) __attribute__((always_inline)) { return lds + (kv * NW + w) * TB; };
+    auto buf_tile = [&](int bi, int x) __attribute__((always_inline)) { return lds + OFF_BUF + (bi * 2 + x) * TB; };
+    auto buf_stat = [&](int bi) __attribute__((always_inline)) {
+        return (float*)(lds + OFF_STAT) + bi * 2 * BLK;
+    };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave >> 2, sub = wave & 3;
     const int l32 = lane & 31, g = lane >> 5;
     const int L = (int)a.L, s = a.s, r = a.r;
     const int G = a.Hq / a.Hkv;
+    // it / G as a multiply-high (exact for it < 2^16, G < 2^16)
+    const uint64_t gmag = (uint64_t)0xFFFFFFFFu / (uint32_t)G + 1;
+    auto div_g = [&](int it) __attribute__((always_inline)) { return (int)(((uint64_t)(uint32_t)it * gmag) >> 32); };
 
     // ---- work item
-    int bhk, tile, seg, nseg_max;
+    int bhk, tile, seg;
     size_t slot_base;
     {
         // sink items (long) first and in their own order, which the
@@ -241,7 +271,6 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
             seg = id % gr.nseg_sink;
             tile = (id / gr.nseg_sink) % gr.tiles_sink;
             bhk = id / (gr.nseg_sink * gr.tiles_sink);
-            nseg_max = gr.nseg_sink;
             slot_base = gr.slots_band + ((size_t)bhk * gr.tiles_sink + tile) * (gr.nseg_sink - 1);
         } else {
             id -= n_sink_items;
@@ -249,11 +278,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
             seg = id % gr.nseg_band;
             tile = gr.tiles_sink + (id / gr.nseg_band) % tb;
             bhk = id / (gr.nseg_band * tb);
-            nseg_max = gr.nseg_band;
             slot_base = ((size_t)bhk * tb + (tile - gr.tiles_sink)) * (gr.nseg_band - 1);
         }
     }
-    (void)nseg_max;
     const int b = bhk / a.Hkv, kvh = bhk % a.Hkv;
     const int i0 = tile * 128, i1 = (i0 + 127) < (L - 1) ? (i0 + 127) : (L - 1);
     // query blocks of the tile: keys i0..i1 are seen by queries i0 .. i1 + r - 1
@@ -265,8 +292,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
     if (sb0 >= nb) return;                                 // an empty segment (all waves leave)
     const int sb1 = (sb0 + gr.segb) < nb ? (sb0 + gr.segb) : nb;
     const int niter = (sb1 - sb0) * G;
+    const int qbase = (qb_lo + sb0) * BLK;                 // first query of the segment
 
-    const int kw0 = i0 + 32 * wave;                        // this wave's keys kw0 .. kw0 + 31
+    const int kw0 = i0 + 32 * sub;                         // this wave's keys kw0 .. kw0 + 31
     const int my_key = kw0 + l32;
     const bool wave_active = kw0 <= i1;
     const __bf16* kg = (const __bf16*)a.k + (size_t)bhk * L * D;
@@ -274,34 +302,36 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
 
     // K and V of the tile's 128 keys stay in LDS for the whole item (the
     // B operands of S = Q K^T and dP = dO V^T: lane takes its key, dims
-    // 16 ks + 8 g .. +7); keys past L are row L-1 (masked)
+    // 16 ks + 8 g .. +7); keys past L are row L-1 (masked).  Group 0
+    // loads K, group 1 V.
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        TT::load(kvs[0][w], kg, i0 + 32 * w, 0, L - 1, wave, lane);
-        TT::load(kvs[1][w], vg, i0 + 32 * w, 0, L - 1, wave, lane);
-    }
-    const char* Kw = kvs[0][wave];
-    const char* Vw = kvs[1][wave];
+    for (int w = 0; w < NW; ++w) TT::load(kv_tile(grp, w), grp ? vg : kg, i0 + 32 * w, 0, L - 1, sub, lane);
+    const char* Kw = kv_tile(0, sub);
+    const char* Vw = kv_tile(1, sub);
 
-    // iteration it: query block qb = qb_lo + sb0 + it / G of q-head kvh * G + it % G
-    auto issue = [&](int it, int buf) __attribute__((always_inline)) {
-        const int qb = qb_lo + sb0 + it / G;
-        const int bhq = b * a.Hq + kvh * G + it % G;
+    // the loads of iteration it into buffer bi, by the four waves of one group
+    auto issue = [&](int it, int bi) __attribute__((always_inline)) {
+        const int qi = div_g(it);
+        const int qb = qb_lo + sb0 + qi;
+        const int bhq = b * a.Hq + kvh * G + (it - qi * G);
         const __bf16* qg = (const __bf16*)a.q + (size_t)bhq * L * D;
         const __bf16* dg = (const __bf16*)a.dout + (size_t)bhq * L * D;
-        TT::load(smem[buf][0], qg, qb * BLK, 0, L - 1, wave, lane);
-        TT::load(smem[buf][1], dg, qb * BLK, 0, L - 1, wave, lane);
+        TT::load(buf_tile(bi, 0), qg, qb * BLK, 0, L - 1, sub, lane);
+        TT::load(buf_tile(bi, 1), dg, qb * BLK, 0, L - 1, sub, lane);
         // lse and D of the block's 32 rows: 4 lanes of every wave, 16 bytes
         // each (rows past L read the next head's values or the arrays'
         // padding; the masks drop them)
         if (lane < 4) {
-            const int x = 4 * wave + lane;                      // 16-byte piece 0..15
+            const int x = 4 * sub + lane;                       // 16-byte piece 0..15
             const float* src = (x < 8 ? a.lse2 : a.dd) + (size_t)bhq * L;
-            load_lds16(src + qb * BLK + 4 * (x & 7), &stat[buf][0][0] + 16 * wave);
+            load_lds16(src + qb * BLK + 4 * (x & 7), buf_stat(bi) + 16 * sub);
         }
     };
-    // loads per wave per iteration: two tiles, one stat piece
-    constexpr int NLD = 2 * TT::JW + 1;
+    // does this wave's key block meet iteration it's query block?
+    auto need_of = [&](int it) __attribute__((always_inline)) {
+        const int tq0 = qbase + BLK * div_g(it);
+        return wave_active && kw0 <= tq0 + BLK - 1 && tq0 <= L - 1 && (kw0 < s || kw0 + BLK - 1 >= tq0 - r + 1);
+    };
 
     f32x16 dvT[NDB], dkT[NDB];
 #pragma unroll
@@ -309,68 +339,102 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
         dvT[db] = f32x16{};
         dkT[db] = f32x16{};
     }
+    f32x16 sa = {}, pa = {};            // S and dP of an iteration, from its C to its X
+    bf16x8 pp[2], ps[2];                // P and dS, from its X to the group's next C
     const float c = a.scale_log2e;
 
-    // (the first wait below also covers the K and V loads, issued before)
-    issue(0, 0);
-    if (niter > 1) issue(1, 1);
-    int buf = 0;
-    for (int it = 0; it < niter; ++it) {
-        wait_vm(it + 1 < niter ? NLD : 0);
-        wg_barrier();
-        if (it + 2 < niter) issue(it + 2, buf == 0 ? 2 : buf - 1);
-        const int tq0 = (qb_lo + sb0 + it / G) * BLK;        // the block's queries tq0 .. tq0 + 31
-        const bool need = wave_active && kw0 <= tq0 + BLK - 1 && tq0 <= L - 1 &&
-                          (kw0 < s || kw0 + BLK - 1 >= tq0 - r + 1);
-        if (need) {
-            const char* Qt = smem[buf][0];
-            const char* Ot = smem[buf][1];   // dO
-            f32x16 sa = {}, pa = {};
+    // iterations 0 and 1 travel with K and V
+    if (grp < niter) issue(grp, grp);
+    wait_vm(0);
+    wg_barrier();
+
+    auto bmod = [](int x) __attribute__((always_inline)) { return x >= PB ? x - PB : x; };
+    int bh = 0;                         // h mod PB
+    for (int h = 0; h < niter + 2; ++h) {
+        if (((h ^ grp) & 1) == 0) {
+            // ---- C: dV/dK of iteration h-2, S/dP of iteration h
+            const int ip = h - 2;
+            if (ip >= 0 && need_of(ip)) {
+                const int bp = bmod(bh + PB - 2);
+                const char* Qp = buf_tile(bp, 0);
+                const char* Op = buf_tile(bp, 1);   // dO
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sa = mfma(TT::rowop(Qt, l32, g, ks), TT::colop(Kw, l32, g, ks), sa);
-                pa = mfma(TT::rowop(Ot, l32, g, ks), TT::colop(Vw, l32, g, ks), pa);
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dvT[db] = mfma(TT::trop(Op, lane, db, kk), pp[kk], dvT[db]);
+                        dkT[db] = mfma(TT::trop(Qp, lane, db, kk), ps[kk], dkT[db]);
+                    }
             }
-            // lse and D of this lane's 16 queries (rows 8g .. 8g+7, 16+8g .. +7),
-            // four at a time: element i takes lq(i) = stat[.][16 (i/8) + 8 g + i%8]
-            const float* ls = &stat[buf][0][0];
-            const float* dd = &stat[buf][1][0];
-            auto lq = [&](int i) __attribute__((always_inline)) { return ls[crow(i, g)]; };
-            auto dq4 = [&](int i) __attribute__((always_inline)) { return dd[crow(i, g)]; };
-            const bool full = kw0 + BLK - 1 <= tq0 && tq0 + BLK - 1 <= L - 1 && kw0 + BLK - 1 <= L - 1 &&
-                              (kw0 + BLK - 1 < s || kw0 >= tq0 + BLK - 1 - r + 1);
-            bf16x8 pp[2], ps[2];
-            if (full) {
+            // P and dS die before S and dP are born (registers)
+            __builtin_amdgcn_sched_barrier(0);
+            if (h < niter && need_of(h)) {
+                const char* Qt = buf_tile(bh, 0);
+                const char* Ot = buf_tile(bh, 1);
+                sa = f32x16{};
+                pa = f32x16{};
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq(i)));
-                    pp[i / 8][i % 8] = (__bf16)p;
-                    ps[i / 8][i % 8] = (__bf16)(p * (pa[i] - dq4(i)));
-                }
-            } else {
-                // masked pairs (and rows past L, whose statistics are not
-                // this head's) give P = dS = 0
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int t = tq0 + crow(i, g);
-                    const bool ok = (t <= L - 1) & (my_key <= L - 1) & in_set(t, my_key, s, r);
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq(i)));
-                    const float dsv = p * (pa[i] - dq4(i));
-                    pp[i / 8][i % 8] = (__bf16)(ok ? p : 0.0f);
-                    ps[i / 8][i % 8] = (__bf16)(ok ? dsv : 0.0f);
+                for (int ks = 0; ks < KS; ++ks) {
+                    sa = mfma(TT::rowop(Qt, l32, g, ks), TT::colop(Kw, l32, g, ks), sa);
+                    pa = mfma(TT::rowop(Ot, l32, g, ks), TT::colop(Vw, l32, g, ks), pa);
                 }
             }
+            // this wave's loads (issued in its last X half-slot) land before
+            // the barrier that precedes their first reader
+            wait_vm(0);
+        } else {
+            // ---- X: softmax of iteration h-1, loads of iteration h+2
+            const int ix = h - 1;
+            if (ix >= 0 && ix < niter && need_of(ix)) {
+                const int tq0 = qbase + BLK * div_g(ix);
+                const float* ls = buf_stat(bmod(bh + PB - 1));
+                const float* dd = ls + BLK;
+                // lse and D of this lane's 16 queries (rows 8g .. 8g+7, 16+8g .. +7)
+                auto lq = [&](int i) __attribute__((always_inline)) { return ls[crow(i, g)]; };
+                auto dq4 = [&](int i) __attribute__((always_inline)) { return dd[crow(i, g)]; };
+                const bool full = kw0 + BLK - 1 <= tq0 && tq0 + BLK - 1 <= L - 1 && kw0 + BLK - 1 <= L - 1 &&
+                                  (kw0 + BLK - 1 < s || kw0 >= tq0 + BLK - 1 - r + 1);
+                if (full) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+                    for (int i = 0; i < 16; ++i) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq(i)));
+                        pp[i / 8][i % 8] = (__bf16)p;
+                        ps[i / 8][i % 8] = (__bf16)(p * (pa[i] - dq4(i)));
+                    }
+                } else {
+                    // masked pairs (and rows past L, whose statistics are
+                    // not this head's) give P = dS = 0
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dvT[db] = mfma(TT::trop(Ot, lane, db, kk), pp[kk], dvT[db]);
-                    dkT[db] = mfma(TT::trop(Qt, lane, db, kk), ps[kk], dkT[db]);
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = tq0 + crow(i, g);
+                        const bool ok = (t <= L - 1) & (my_key <= L - 1) & in_set(t, my_key, s, r);
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[i], c, -lq(i)));
+                        const float dsv = p * (pa[i] - dq4(i));
+                        pp[i / 8][i % 8] = (__bf16)(ok ? p : 0.0f);
+                        ps[i / 8][i % 8] = (__bf16)(ok ? dsv : 0.0f);
+                    }
                 }
+            }
+            if (h + 2 < niter) issue(h + 2, bmod(bh + 2));
         }
-        buf = buf == 2 ? 0 : buf + 1;
+        wg_barrier();
+        bh = bmod(bh + 1);
     }
-    if (!wave_active || my_key > L - 1) return;
+
+    // group 1 hands its sums to group 0 (the buffers are free: every load
+    // landed before the last barrier and every read is behind it)
+    float* red = (float*)lds + (size_t)sub * (2 * NDB * 16 * 64) + lane;
+    if (grp == 1) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                red[((2 * db) * 16 + i) * 64] = dkT[db][i];
+                red[((2 * db + 1) * 16 + i) * 64] = dvT[db][i];
+            }
+    }
+    wg_barrier();
+    if (grp == 1 || !wave_active || my_key > L - 1) return;
     // segment 0 stores the sums, the others partial sums for bwd_reduce
     float *dk, *dv;
     if (seg == 0) {
@@ -381,19 +445,24 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(BackwardArgs a, BwdGrid
         dk = slot + (size_t)(my_key - i0) * D;
         dv = slot + (size_t)(128 + my_key - i0) * D;
     }
+    // one 32-dim block at a time (the partner's values and the sums of one
+    // block in registers at once)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             f32x4 xk, xv;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                xk[j] = dkT[db][4 * q4 + j] * a.scale;
-                xv[j] = dvT[db][4 * q4 + j];
+                const int i = 4 * q4 + j;
+                xk[j] = (dkT[db][i] + red[((2 * db) * 16 + i) * 64]) * a.scale;
+                xv[j] = dvT[db][i] + red[((2 * db + 1) * 16 + i) * 64];
             }
             *(f32x4*)(dk + 32 * db + 8 * q4 + 4 * g) = xk;
             *(f32x4*)(dv + 32 * db + 8 * q4 + 4 * g) = xv;
         }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Adds the partial sums of segments 1 .. of every split key tile to dK and
@@ -435,7 +504,7 @@ hipError_t launch(const BackwardArgs& a, const BwdGrid& gr, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t items = (int64_t)gr.bhkv * (gr.tiles_sink * gr.nseg_sink + (gr.tiles - gr.tiles_sink) * gr.nseg_band);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)items), dim3(NT), 0, st, a, gr);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)items), dim3(2 * NT), 0, st, a, gr);
     e = hipGetLastError();
     if (e != hipSuccess || gr.slots_band + gr.slots_sink == 0) return e;
     const int64_t n = (int64_t)gr.bhkv * a.L * (D / 4);
