@@ -12,27 +12,28 @@
 // with dK and dV summed over the q-heads of a kv-head.
 //
 // Two kernels, both tiled in 32x32 blocks on v_mfma_f32_32x32x16_bf16, with
-// the block operands staged in LDS by direct global->LDS loads (three
-// buffer sets, loads two blocks ahead):
+// the block operands staged in LDS by direct global->LDS loads:
 //
-//   bwd_dq (query-outer, like the forward): a wave owns 32 query rows with
-//     q and dO in registers and walks the key blocks of their key sets
-//     (the sink block, then the band; blocks outside are never loaded):
+//   bwd_dq (query-outer, like the forward; 4 waves, three buffer sets
+//     loaded two blocks ahead): a wave owns 32 query rows with q and dO in
+//     registers and walks the key blocks of their key sets (the sink
+//     block, then the band; blocks outside are never loaded):
 //       S^T = K Q^T and dP^T = V dO^T (16 MFMAs), an online softmax over
 //       the keys (running max lazily raised, as in the forward), dS^T =
 //       P^T (dP^T - D) packed to bf16, dQ^T += K^T dS^T (8 MFMAs, K read
 //       transposed from LDS).  It also writes the row's log-sum-exp and
 //       D_t for the second kernel.
-//   bwd_dkdv (key-outer): a wave owns 32 keys with K and V in registers
-//     and walks the 32-row query blocks of every q-head of the kv-head
-//     that see them: S = Q K^T and dP = dO V^T (16 MFMAs), P from the
-//     row's log-sum-exp, dS = P (dP - D), then dV^T += dO^T P and dK^T +=
-//     Q^T dS (16 MFMAs, Q and dO read transposed from LDS).  A key tile
-//     (128 keys, four waves) whose queries span more than one segment is
-//     split into segments; segment 0 stores its sums, the others store
-//     partial sums that bwd_reduce adds in a fixed order (sink keys see
-//     every later query, so their tiles take many segments).  No atomics:
-//     the gradients are the same on every call.
+//   bwd_dkdv (key-outer; 8 waves in two groups that alternate on the
+//     SIMDs): a wave owns 32 keys of the tile's 128, whose K and V stay in
+//     LDS, and every other 32-row query block of the q-heads of the
+//     kv-head that see them: S = Q K^T and dP = dO V^T (16 MFMAs), P from
+//     the row's log-sum-exp, dS = P (dP - D), then dV^T += dO^T P and dK^T
+//     += Q^T dS (16 MFMAs, Q and dO read transposed from LDS).  A key tile
+//     whose queries span more than one segment is split into segments;
+//     segment 0 stores its sums, the others store partial sums that
+//     bwd_reduce adds in a fixed order (sink keys see every later query,
+//     so their tiles take many segments).  No atomics: the gradients are
+//     the same on every call.
 //
 // Rows of an MFMA block enter in the order swap23(m) (bits 2 and 3 of the
 // row index swapped), so that each lane's eight accumulator values of one
