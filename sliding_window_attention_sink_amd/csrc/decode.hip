@@ -35,6 +35,10 @@
 //    current token's slot first writes the token's K/V row there (then
 //    waits for the stores and a barrier), so one launch does the append and
 //    the decode.
+//  * several query rows at once (npos > 0, the dense rows of task-bound
+//    global tokens): the q-heads of npos positions take G * npos <= 16
+//    query columns, and column (pi, head) keeps only the keys <= pos[pi],
+//    so each K/V byte is read once for all of them.
 #include <mutex>
 
 #include "rope_common.h"
@@ -101,7 +105,7 @@ struct DecodeSmem {
 
 __device__ __forceinline__ int vswz(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool MULTI>
 __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     __shared__ DecodeSmem<D> sm;
     constexpr int CH = D / 8;            // 16-byte chunks per row
@@ -155,15 +159,22 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     };
 
     // Q^T operand: column col = q-head kvh*G + col (zero past the group);
-    // with RoPE columns G .. 2G-1 hold the same heads rotated for the sinks
+    // with RoPE columns G .. 2G-1 hold the same heads rotated for the sinks;
+    // with several positions column col is head col % G of row pos[col / G]
     constexpr int HK = KSTEPS / 2;
     constexpr bool rope = ROPE;
+    const int ncol = MULTI ? G * a.npos : G;
+    const int col_pi = MULTI ? col / G : 0;
+    const int col_head = MULTI ? col - col_pi * G : col;
+    // this lane's column sees keys up to lim (several positions)
+    const int lim = MULTI ? (col < ncol ? a.pos[col_pi] : -1) : 0;
     bf16x8 qreg[KSTEPS];
     {
-        const bool qband = col < G;
+        const bool qband = col < ncol;
         const bool qsink = rope && col >= G && col < 2 * G;
-        const int head = qband ? col : (qsink ? col - G : 0);
-        const __bf16* qrow = (const __bf16*)a.q + ((size_t)b * a.Hq + kvh * G + head) * a.qo_stride;
+        const int head = qband ? col_head : (qsink ? col - G : 0);
+        const __bf16* qrow = (const __bf16*)a.q + ((size_t)b * a.Hq + kvh * G + head) * a.qo_stride +
+                             (MULTI && qband ? (size_t)a.pos[col_pi] * D : 0);
         u32x4 x[KSTEPS];
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
@@ -185,12 +196,13 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
 
     // one step's K (MFMA operand order) and V rows in registers; without
     // RoPE two such buffers keep two steps of loads in flight per wave (with
-    // RoPE the sink-score exchange needs the registers of the second)
+    // RoPE the sink-score exchange, with several positions the per-column
+    // limits, need the registers of the second)
     struct StepRegs {
         u32x4 k[2][KSTEPS];
         u32x4 v[KPL];
     };
-    constexpr int DEPTH = ROPE ? 1 : 2;
+    constexpr int DEPTH = (ROPE || MULTI) ? 1 : 2;
     // K and V are streamed with the non-temporal hint: every cache byte is
     // read once per step, so keeping it out of the caches leaves them to the
     // reads that do repeat (measured on the 64-sequence workload: 6.7 TB/s
@@ -265,6 +277,14 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
                 for (int i = 0; i < 4; ++i)
                     if (!valid(kb + 8 * g + 4 * bb + i)) sacc[bb][i] = -__builtin_inff();
         }
+        if (MULTI && kb + KW - 1 > a.pos[0]) {
+            // past the first row's limit: each column keeps its own keys
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kb + 8 * g + 4 * bb + i > lim) sacc[bb][i] = -__builtin_inff();
+        }
         float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                          fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     __syncthreads();
 
     // merge the 4 waves: thread -> (column, dim)
-    for (int idx = tid; idx < G * D; idx += NT) {
+    for (int idx = tid; idx < ncol * D; idx += NT) {
         const int cl = idx / D, dim = idx % D;
         float M = sm.m[0][cl];
 #pragma unroll
@@ -340,12 +360,15 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
             o += f * sm.o[w][cl][dim];
             l += f * sm.l[w][cl];
         }
+        // output row and partial-result row of column cl
+        const int cpi = MULTI ? cl / G : 0, chead = MULTI ? cl - cpi * G : cl;
+        const size_t bhq = (size_t)b * a.Hq + kvh * G + chead;
         if (a.n_split == 1) {
             // one split: this workgroup saw every slot, so it finishes the head
-            ((__bf16*)a.o)[((size_t)b * a.Hq + kvh * G + cl) * a.qo_stride + dim] = (__bf16)(o / l);
+            ((__bf16*)a.o)[bhq * a.qo_stride + (MULTI ? (size_t)a.pos[cpi] * D : 0) + dim] = (__bf16)(o / l);
             continue;
         }
-        float* ws = a.ws + (((size_t)b * a.Hq + kvh * G + cl) * a.n_split + split) * (D + 2);
+        float* ws = a.ws + (((MULTI ? bhq * a.npos + cpi : bhq)) * a.n_split + split) * (D + 2);
         if (dim == 0) {
             ws[0] = M;
             ws[1] = l;
@@ -354,9 +377,9 @@ __global__ __launch_bounds__(NT, 2) void decode_split_kernel(DecodeArgs a) {
     }
 }
 
-template <int D>
+template <int D, bool MULTI>
 __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
-    const int bh = blockIdx.x;     // b * Hq + h
+    const int bh = blockIdx.x;     // b * Hq + h (with several positions: (b * Hq + h) * npos + pi)
     const int dim = threadIdx.x;
     const float* ws = a.ws + (size_t)bh * a.n_split * (D + 2);
     float M = -__builtin_inff();
@@ -368,19 +391,30 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
         l += f * ws[k * (D + 2) + 1];
         o += f * ws[k * (D + 2) + 2 + dim];
     }
-    ((__bf16*)a.o)[(size_t)bh * a.qo_stride + dim] = (__bf16)(o / l);
+    if (MULTI) {
+        const int pi = bh % a.npos;
+        ((__bf16*)a.o)[(size_t)(bh / a.npos) * a.qo_stride + (size_t)a.pos[pi] * D + dim] = (__bf16)(o / l);
+    } else {
+        ((__bf16*)a.o)[(size_t)bh * a.qo_stride + dim] = (__bf16)(o / l);
+    }
 }
 
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
     const unsigned nblk = (unsigned)a.B * a.Hkv * a.n_split;
-    if (a.rope_rr > 0.0)
-        hipLaunchKernelGGL((decode_split_kernel<D, true>), dim3(nblk), dim3(NT), 0, st, a);
+    const bool multi = a.npos > 0;
+    if (multi)
+        hipLaunchKernelGGL((decode_split_kernel<D, false, true>), dim3(nblk), dim3(NT), 0, st, a);
+    else if (a.rope_rr > 0.0)
+        hipLaunchKernelGGL((decode_split_kernel<D, true, false>), dim3(nblk), dim3(NT), 0, st, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<D, false>), dim3(nblk), dim3(NT), 0, st, a);
+        hipLaunchKernelGGL((decode_split_kernel<D, false, false>), dim3(nblk), dim3(NT), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
-    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((unsigned)a.B * a.Hq), dim3(D), 0, st, a);
+    if (multi)
+        hipLaunchKernelGGL((decode_reduce_kernel<D, true>), dim3((unsigned)a.B * a.Hq * a.npos), dim3(D), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_reduce_kernel<D, false>), dim3((unsigned)a.B * a.Hq), dim3(D), 0, st, a);
     return hipGetLastError();
 }
 

@@ -307,7 +307,8 @@ GlobalLayout global_layout(const swa_desc* d, int64_t L) {
     x.vg = round_up(kgb, 256);
     x.lse = x.vg + round_up(kgb, 256);
     x.part = x.lse + round_up((size_t)d->B * d->Hq * (size_t)L * sizeof(float), 256);
-    x.total = x.part + round_up(decode_ws_bytes(&x.dense, x.n_split), 256);
+    // partial results of the batched dense rows: up to 16 positions a launch
+    x.total = x.part + round_up(16 * decode_ws_bytes(&x.dense, x.n_split), 256);
     return x;
 }
 
@@ -376,21 +377,23 @@ int swa_prefill_global(const swa_desc* desc, const void* q, const void* k, const
                            stream)))
         return st;
     if ((st = hip_status(swa::launch_global_merge_bf16(ga, desc->d, hs), fn))) return st;
-    // the global rows: dense causal rows over keys 0 .. t
+    // the global rows: dense causal rows over keys 0 .. t, 16 / G positions
+    // a launch as extra query columns (each K/V byte read once per launch)
     const int S = (int)L;
     int sps = (S + lay.n_split - 1) / lay.n_split;
     sps = (sps + 31) / 32 * 32;
-    for (int32_t j = 0; j < ng; ++j) {
-        const int64_t t = globals[j];
+    const int per = 16 / (desc->Hq / desc->Hkv);
+    for (int32_t j0 = 0; j0 < ng; j0 += per) {
+        const int np = (ng - j0) < per ? (ng - j0) : per;
         swa::DecodeArgs da{};
-        da.q = static_cast<const __bf16*>(q) + t * desc->d;
+        da.q = q;
         da.kc = k;
         da.vc = v;
-        da.o = static_cast<__bf16*>(o) + t * desc->d;
+        da.o = o;
         da.ws = reinterpret_cast<float*>(ws + lay.part);
         da.kn = nullptr;
         da.vn = nullptr;
-        da.T = t + 1;
+        da.T = (int64_t)globals[j0 + np - 1] + 1;
         da.j_new = -1;
         da.rope_rr = 0.0;
         da.qo_stride = L * desc->d;
@@ -402,6 +405,8 @@ int swa_prefill_global(const swa_desc* desc, const void* q, const void* k, const
         da.n_split = lay.n_split;
         da.slots_per_split = sps;
         da.scale_log2e = ga.scale_log2e;
+        da.npos = np;
+        for (int i = 0; i < np; ++i) da.pos[i] = globals[j0 + i];
         if ((st = hip_status(swa::launch_decode_bf16(da, desc->d, hs), fn))) return st;
     }
     return SWA_OK;

@@ -77,6 +77,12 @@ struct DecodeArgs {
     int32_t n_split;
     int32_t slots_per_split;
     float scale_log2e;
+    // npos > 0: the query rows of npos positions at once (G * npos <= 16, no
+    // RoPE): row (b, h, pos[pi]) of q and o sits at (b Hq + h) qo_stride +
+    // pos[pi] d and sees keys (slots) 0 .. pos[pi]; pos ascending, T =
+    // pos[npos-1] + 1; ws is [B, Hq, npos, n_split, d + 2]
+    int32_t npos;
+    int32_t pos[16];
 };
 
 // Rows [rows, d] of keys for positions pos0 + (row mod n) (the rows of

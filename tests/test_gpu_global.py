@@ -28,6 +28,10 @@ CASES = [
     (1, 2, 2, 128, 130, 4, 200, [10, 60]),                      # window covers everything
     (1, 4, 4, 64, 1000, 30, 1, [29, 30, 31, 500, 999]),         # r = 1, globals at the sink edge
     (2, 2, 1, 128, 65, 70, 10, [3, 64]),                        # sinks beyond L
+    # dense global rows batched 16 / (q-heads per kv-head) positions a launch
+    (1, 2, 2, 128, 500, 4, 32, list(range(7, 500, 25))),       # 20 rows: launches of 16 + 4
+    (1, 8, 1, 128, 333, 0, 50, [0, 100, 332]),                  # 8 q-heads: 2 + 1, a row at 0
+    (1, 16, 1, 64, 200, 2, 30, [1, 40, 41, 199]),               # 16 q-heads: one position a launch
 ]
 
 
