@@ -155,10 +155,12 @@ int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, c
  * global positions g <= t, each key once (a global among the sinks or inside
  * the window adds nothing).  Layouts as for swa_prefill without a cache;
  * bf16, no RoPE, up to 16 q-heads per kv-head.  ng = 0 is swa_prefill.
- * Runs the banded prefill, then merges each row with its global keys through
- * the two softmax normalisers, then computes the global rows as dense
- * causal rows.  Workspace: swa_prefill_global_workspace_bytes(desc, L, ng)
- * bytes (global keys and values, the rows' log-sum-exp, split partials).
+ * Gathers the global keys and values into one 64-key block, runs the banded
+ * prefill with that block as one more key tile (each row keeps the globals
+ * outside its key set), then computes the global rows as dense causal rows,
+ * 16 / (Hq/Hkv) of them per decode launch.  Workspace:
+ * swa_prefill_global_workspace_bytes(desc, L, ng) bytes (the gathered keys
+ * and values, the dense rows' split partials).
  * Errors: those of swa_prefill, SWA_ERR_INVALID_ARG for bad globals or a
  * short workspace, SWA_ERR_UNSUPPORTED for fp32, RoPE or wide GQA groups.
  */

@@ -57,6 +57,12 @@ SPILL_OK = {
     # (64 VGPRs) spills a few values; fp32 is the precision path, bf16 the
     # performance path
     "_ZN3swa12_GLOBAL__N_114prefill_kernelIfLi128EEEvNS_11PrefillArgsE",
+    # the bf16 prefill with the global-key tile at d = 128 (task-bound
+    # global tokens only): the tile after the band keeps the running max
+    # alive through the band's last products, and two values held across the
+    # band go to scratch (one reloaded in the masked-tile path); the plain
+    # kernel, which every other call runs, has no spill
+    "_ZN3swa12_GLOBAL__N_117prefill_pp_kernelILi128ELb1EEEvNS_11PrefillArgsE",
 }
 
 

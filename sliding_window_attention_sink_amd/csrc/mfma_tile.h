@@ -1,6 +1,5 @@
 // 32x32 MFMA block tiles in LDS and their operand reads, shared by the
-// gfx950 kernels that tile on v_mfma_f32_32x32x16_bf16 with 4-wave
-// workgroups (the backward, the global-token merge).
+// gfx950 backward kernels, which tile on v_mfma_f32_32x32x16_bf16.
 //
 // Rows of an MFMA block enter in the order swap23(m) (bits 2 and 3 of the
 // row index swapped), so that each lane's eight accumulator values of one

@@ -311,7 +311,7 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int D>
+template <int D, bool GLB>
 __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     typedef PP<D> T;
     __shared__ typename T::Buf smem[NSET];
@@ -594,11 +594,53 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // X(v): online softmax of tile v's scores into pk (zeros when no row of
     // the wave needs the tile); the mask is applied only to tiles that are
     // not inside every row's key set.
+    // online softmax of a tile's (masked) scores sacc0/sacc1 into pk
+    auto softmax = [&]() __attribute__((always_inline)) {
+        const float NEG = -__builtin_inff();
+        // P against the running max first: while this lane's weights of the
+        // tile sum to at most 2^8 (so each is at most 2^8, as the lazily
+        // raised max allows anyway) they stand and the tile needs no row
+        // max.  Otherwise, and while a row has no running max yet, the exact
+        // row max is taken, the running state rescaled and P recomputed.
+        float t = 0.0f;
+        bool slow = __builtin_amdgcn_ballot_w64(m_c == NEG) != 0;
+        if (!slow) {
+            const float mneg = -m_c;
+            pk[0] = T::pack8(sacc0, 0, c, mneg, t);
+            pk[1] = T::pack8(sacc0, 8, c, mneg, t);
+            pk[2] = T::pack8(sacc1, 0, c, mneg, t);
+            pk[3] = T::pack8(sacc1, 8, c, mneg, t);
+            slow = __builtin_amdgcn_ballot_w64(!(t <= 256.0f)) != 0;
+        }
+        if (slow) {
+            float mx = T::max2x16(sacc0, sacc1);
+            mx = max_pair_lanes(mx);
+            const float mxc = mx * c;
+            const bool upd = mxc > m_c;
+            if (__builtin_amdgcn_ballot_w64(upd)) {
+                const float alpha = upd ? __builtin_amdgcn_exp2f(m_c - mxc) : 1.0f;
+                m_c = upd ? mxc : m_c;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            }
+            const float mneg = (m_c == NEG) ? 0.0f : -m_c;
+            t = 0.0f;
+            pk[0] = T::pack8(sacc0, 0, c, mneg, t);
+            pk[1] = T::pack8(sacc0, 8, c, mneg, t);
+            pk[2] = T::pack8(sacc1, 0, c, mneg, t);
+            pk[3] = T::pack8(sacc1, 8, c, mneg, t);
+        }
+        l_part += t;
+    };
     auto cluster_x = [&](int v) __attribute__((always_inline)) {
         const float NEG = -__builtin_inff();
-        // tiles in [vx_lo, vx_hi] are needed and mask-free for every row of
-        // the wave; only the others are classified here
         if (v < vx_lo || v > vx_hi) {
+            // tiles in [vx_lo, vx_hi] are needed and mask-free for every row
+            // of the wave; only the others are classified here (the masks
+            // leave the scores of the kept keys; softmax() follows)
             const Phase P = phase_of(v);
             const int kb = tile_of(v) * BN;
             const int lo_w0 = P.band_lo > tw0 - r + 1 ? P.band_lo : tw0 - r + 1;
@@ -643,43 +685,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
                 }
             }
         }
-        // P against the running max first: while this lane's weights of the
-        // tile sum to at most 2^8 (so each is at most 2^8, as the lazily
-        // raised max allows anyway) they stand and the tile needs no row
-        // max.  Otherwise, and while a row has no running max yet, the exact
-        // row max is taken, the running state rescaled and P recomputed.
-        float t = 0.0f;
-        bool slow = __builtin_amdgcn_ballot_w64(m_c == NEG) != 0;
-        if (!slow) {
-            const float mneg = -m_c;
-            pk[0] = T::pack8(sacc0, 0, c, mneg, t);
-            pk[1] = T::pack8(sacc0, 8, c, mneg, t);
-            pk[2] = T::pack8(sacc1, 0, c, mneg, t);
-            pk[3] = T::pack8(sacc1, 8, c, mneg, t);
-            slow = __builtin_amdgcn_ballot_w64(!(t <= 256.0f)) != 0;
-        }
-        if (slow) {
-            float mx = T::max2x16(sacc0, sacc1);
-            mx = max_pair_lanes(mx);
-            const float mxc = mx * c;
-            const bool upd = mxc > m_c;
-            if (__builtin_amdgcn_ballot_w64(upd)) {
-                const float alpha = upd ? __builtin_amdgcn_exp2f(m_c - mxc) : 1.0f;
-                m_c = upd ? mxc : m_c;
-                l_part *= alpha;
-#pragma unroll
-                for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-            }
-            const float mneg = (m_c == NEG) ? 0.0f : -m_c;
-            t = 0.0f;
-            pk[0] = T::pack8(sacc0, 0, c, mneg, t);
-            pk[1] = T::pack8(sacc0, 8, c, mneg, t);
-            pk[2] = T::pack8(sacc1, 0, c, mneg, t);
-            pk[3] = T::pack8(sacc1, 8, c, mneg, t);
-        }
-        l_part += t;
+        softmax();
     };
 
     // ---- schedule.  Half-slot hs: group 0 runs C(v) at hs = 2v and X(v) at
@@ -792,6 +798,48 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         }
     }
 
+    // Task-bound global tokens: the gathered global keys at or past s (kc /
+    // vc point at the [64, d] blocks in calls with globals) as one more tile
+    // after the band, once per item with no ping-pong: row t keeps rows 0 ..
+    // gjb[t]-1 of the block, the globals below its window.
+    if constexpr (GLB) {
+        if (nv > 0 && __builtin_amdgcn_readfirstlane((int)a.gjb[t1]) > 0) {
+            wait_vm(0);
+            wg_barrier();                  // every tile read is done: set 0 is free
+            {
+                // group 0 loads K, group 1 V (rows 0 .. 63, contiguous; a
+                // call with globals has rs = d, so the own-row offsets fit)
+                const bool is_k = grp == 0;
+                const __bf16* base = is_k ? kc : vc;
+                u32x4* dst0 = is_k ? smem[0].k : smem[0].v;
+#pragma unroll
+                for (int j = 0; j < T::JN; ++j)
+                    load_lds16_off(base + (size_t)T::JSTEP * j * D, is_k ? kloff : vloff, dst0 + 64 * (sub + GW * j));
+            }
+            wait_vm(0);
+            wg_barrier();
+            if (wave_active && __builtin_amdgcn_readfirstlane((int)a.gjb[tw1]) > 0) {
+                // lane-derived offsets formed again here (held across the
+                // band's last products they would cost registers there)
+                int ln = (int)threadIdx.x & 63;
+                asm volatile("" : "+v"(ln));
+                int gbe, gbo;
+                T::k_rd_bases(ln & 31, ln >> 5, gbe, gbo);
+                T::template cluster<true, false>(smem[0], qr, vb, pk, gbe, gbo, sacc0, sacc1, oacc, [] {});
+                const int tt = tw0 + (ln & 31);
+                const int lim = (int)a.gjb[tt < t1 ? tt : t1] - 8 * (ln >> 5);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int k0 = keyoff(i, 0), k1 = 32 + keyoff(i, 0);
+                    sacc0[i] = k0 < lim ? sacc0[i] : -__builtin_inff();
+                    sacc1[i] = k1 < lim ? sacc1[i] : -__builtin_inff();
+                }
+                softmax();
+                T::template cluster<false, true>(smem[0], qr, vb, pk, kbe, kbo, sacc0, sacc1, oacc, [] {});
+            }
+        }
+    }
+
     // the buffers take the output rows once every load has landed and every
     // wave is past its last read
     wait_vm(0);
@@ -801,8 +849,6 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     static_assert(PW * WROWS * T::ORS <= (int)sizeof(smem), "output staging fits the tile buffers");
     T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * rs, rsb, oacc,
                my_valid ? 1.0f / l_tot : 0.0f, lane, tw1 - tw0 + 1);
-    if (a.lse != nullptr && my_valid && g == 0)
-        a.lse[(size_t)(b * a.Hq + h) * a.L + wrow0 + l32] = m_c + __builtin_amdgcn_logf(l_tot);
 }
 
 template <int D>
@@ -810,7 +856,10 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
     const long long G = a.Hq / a.Hkv;
     const long long nblk = a.pair_mode ? (long long)a.B * a.Hkv * (G / 2) * a.n_mtiles
                                        : (long long)a.B * a.Hq * a.n_mtiles;
-    hipLaunchKernelGGL((prefill_pp_kernel<D>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
+    if (a.ng > 0)
+        hipLaunchKernelGGL((prefill_pp_kernel<D, true>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
+    else
+        hipLaunchKernelGGL((prefill_pp_kernel<D, false>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
     return hipGetLastError();
 }
 

@@ -141,7 +141,6 @@ size_t swa_prefill_workspace_bytes(const swa_desc* desc, int64_t L) {
 
 namespace {
 
-// swa_prefill; lse (null or [B, Hq, L]) receives each row's log2-sum-exp.
 // Query tiles per (batch, q-head) for L rows
 int64_t prefill_mtiles(const swa_desc* desc, int64_t L) {
     const int64_t rows_per_block = desc->dtype == SWA_BF16 ? swa::prefill_bf16_rows_per_block(desc->Hq, desc->Hkv)
@@ -184,8 +183,9 @@ hipError_t launch_prefill(const swa_desc* desc, const swa::PrefillArgs& a, hipSt
     return desc->dtype == SWA_BF16 ? swa::launch_prefill_bf16(a, desc->d, hs) : swa::launch_prefill_f32(a, desc->d, hs);
 }
 
+// swa_prefill
 int prefill_impl(const char* fn, const swa_desc* desc, const void* q, const void* k, const void* v, void* o,
-                 int64_t L, const void* k_cache, const void* v_cache, int64_t pos0, float* lse, void* stream) {
+                 int64_t L, const void* k_cache, const void* v_cache, int64_t pos0, void* stream) {
     clear_error();
     int st = check_desc(desc, fn);
     if (st) return st;
@@ -212,7 +212,6 @@ int prefill_impl(const char* fn, const swa_desc* desc, const void* q, const void
         a.merge_sink = 0;
         a.rope_rr = rope_rr(desc);
     }
-    a.lse = lse;
     return hip_status(launch_prefill(desc, a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
@@ -225,7 +224,7 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
                 void* stream) {
     (void)workspace;         // no prefill kernel uses one (swa_prefill_workspace_bytes is 0)
     (void)workspace_bytes;
-    return prefill_impl("swa_prefill", desc, q, k, v, o, L, k_cache, v_cache, pos0, nullptr, stream);
+    return prefill_impl("swa_prefill", desc, q, k, v, o, L, k_cache, v_cache, pos0, stream);
 }
 
 int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new, int64_t n, int64_t pos0,
@@ -290,7 +289,7 @@ namespace {
 struct GlobalLayout {
     swa_desc dense{};
     int32_t n_split = 1;
-    size_t kg = 0, vg = 0, lse = 0, part = 0, total = 0;
+    size_t kg = 0, vg = 0, jb = 0, part = 0, total = 0;
 };
 
 GlobalLayout global_layout(const swa_desc* d, int64_t L) {
@@ -305,8 +304,8 @@ GlobalLayout global_layout(const swa_desc* d, int64_t L) {
     const size_t kgb = (size_t)d->B * d->Hkv * swa::kMaxGlobals * d->d * 2;
     x.kg = 0;
     x.vg = round_up(kgb, 256);
-    x.lse = x.vg + round_up(kgb, 256);
-    x.part = x.lse + round_up((size_t)d->B * d->Hq * (size_t)L * sizeof(float), 256);
+    x.jb = x.vg + round_up(kgb, 256);
+    x.part = x.jb + round_up((size_t)L, 256);
     // partial results of the batched dense rows: up to 16 positions a launch
     x.total = x.part + round_up(16 * decode_ws_bytes(&x.dense, x.n_split), 256);
     return x;
@@ -354,29 +353,28 @@ int swa_prefill_global(const swa_desc* desc, const void* q, const void* k, const
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
+    // the globals at or past s, gathered into one 64-key block per (batch,
+    // kv-head), with each row's count of them below its window
     swa::GlobalArgs ga{};
-    ga.q = q;
     ga.k = k;
     ga.v = v;
-    ga.o = o;
     ga.kg = ws + lay.kg;
     ga.vg = ws + lay.vg;
-    ga.lse = reinterpret_cast<const float*>(ws + lay.lse);
+    ga.gjb = reinterpret_cast<uint8_t*>(ws + lay.jb);
     ga.L = L;
     ga.B = desc->B;
-    ga.Hq = desc->Hq;
     ga.Hkv = desc->Hkv;
-    ga.s = desc->s;
     ga.r = desc->r;
-    ga.ng = ng;
-    ga.scale_log2e = (float)((double)desc->scale * 1.4426950408889634);
-    for (int32_t j = 0; j < ng; ++j) ga.pos[j] = globals[j];
+    for (int32_t j = 0; j < ng; ++j)
+        if (globals[j] >= desc->s) ga.pos[ga.ng++] = globals[j];
     if ((st = hip_status(swa::launch_global_gather_bf16(ga, desc->d, hs), fn))) return st;
-    // the banded rows, with their log-sum-exp
-    if ((st = prefill_impl(fn, desc, q, k, v, o, L, nullptr, nullptr, 0, reinterpret_cast<float*>(ws + lay.lse),
-                           stream)))
-        return st;
-    if ((st = hip_status(swa::launch_global_merge_bf16(ga, desc->d, hs), fn))) return st;
+    // the banded rows, with those globals as one more key tile
+    swa::PrefillArgs pa = dense_prefill_args(desc, q, k, v, o, L, ws + lay.kg, ws + lay.vg, 0);
+    pa.c_bh = (int64_t)swa::kMaxGlobals * desc->d;
+    pa.gjb = reinterpret_cast<const uint8_t*>(ws + lay.jb);
+    pa.ng = ga.ng;
+    if (ga.ng > 0 && (st = hip_status(launch_prefill(desc, pa, hs), fn))) return st;
+    if (ga.ng == 0 && (st = prefill_impl(fn, desc, q, k, v, o, L, nullptr, nullptr, 0, stream))) return st;
     // the global rows: dense causal rows over keys 0 .. t, 16 / G positions
     // a launch as extra query columns (each K/V byte read once per launch)
     const int S = (int)L;
@@ -404,7 +402,7 @@ int swa_prefill_global(const swa_desc* desc, const void* q, const void* k, const
         da.r = lay.dense.r;
         da.n_split = lay.n_split;
         da.slots_per_split = sps;
-        da.scale_log2e = ga.scale_log2e;
+        da.scale_log2e = pa.scale_log2e;
         da.npos = np;
         for (int i = 0; i < np; ++i) da.pos[i] = globals[j0 + i];
         if ((st = hip_status(swa::launch_decode_bf16(da, desc->d, hs), fn))) return st;
@@ -433,7 +431,7 @@ int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, c
     if (desc->rope_base > 0.0f) return fail(SWA_ERR_UNSUPPORTED, "%s: dilation with RoPE is not built", fn);
     // with L <= s every row is a sink row (keys 0 .. t), the plain window's rows
     if (dilation == 1 || L <= desc->s)
-        return prefill_impl(fn, desc, q, k, v, o, L, nullptr, nullptr, 0, nullptr, stream);
+        return prefill_impl(fn, desc, q, k, v, o, L, nullptr, nullptr, 0, stream);
     if ((st = check_ptr(q, fn, "q")) || (st = check_ptr(k, fn, "k")) || (st = check_ptr(v, fn, "v")) ||
         (st = check_ptr(o, fn, "o")))
         return st;

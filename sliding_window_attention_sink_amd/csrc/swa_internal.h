@@ -44,9 +44,15 @@ struct PrefillArgs {
     // token's position; the kernel rotates the queries, at t for window keys
     // and at min(t, s+r-1) for sinks.  rope_rr = base^(-2/d).
     double rope_rr;
-    // null, or [B, Hq, L]: each row's log2-sum-exp of its scaled scores
-    // (scale * log2(e) units), for merging further keys into the row
-    float* lse;
+    // Task-bound global tokens (ng > 0; bf16 kernel, no RoPE; kc / vc then
+    // point at the [B Hkv, 64, d] blocks, c_bh = 64 d, pos0 = 0): the keys
+    // and values of the global positions g >= s, in order, form one more key
+    // tile after the band, and row t keeps rows 0 .. gjb[t]-1 of it, the
+    // globals below its window (gjb[t] = #{g : s <= g < t - r + 1}; the
+    // globals below s are sinks already, those from t - r + 1 on are in the
+    // window or in the future).
+    const uint8_t* gjb;   // [L]
+    int32_t ng;
 };
 
 struct AppendArgs {
@@ -98,20 +104,16 @@ struct RopeKeysArgs {
 // positions, passed by value.
 constexpr int kMaxGlobals = 64;
 struct GlobalArgs {
-    const void* q;      // [B, Hq, L, d]
     const void* k;      // [B, Hkv, L, d]
     const void* v;
-    void* o;            // [B, Hq, L, d]: the banded rows, merged in place
     void* kg;           // workspace [B * Hkv, kMaxGlobals, d]: keys of the global positions
     void* vg;           // ... values
-    const float* lse;   // [B, Hq, L]: the banded rows' log2-sum-exp (scale * log2(e) units)
+    uint8_t* gjb;       // workspace [L]: gjb[t] = #{j : pos[j] < t - r + 1}
     int64_t L;
-    int32_t B, Hq, Hkv, s, r, ng;
-    float scale_log2e;
+    int32_t B, Hkv, r, ng;   // pos[0 .. ng-1]: the global positions >= s, ascending
     int32_t pos[kMaxGlobals];
 };
 hipError_t launch_global_gather_bf16(const GlobalArgs& a, int d, hipStream_t st);
-hipError_t launch_global_merge_bf16(const GlobalArgs& a, int d, hipStream_t st);
 
 // Query rows per workgroup of the bf16 prefill kernel for this head layout.
 int prefill_bf16_rows_per_block(int Hq, int Hkv);
