@@ -359,13 +359,21 @@ __global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, Bwd
                 const int bp = bmod(bh + PB - 2);
                 const char* Qp = buf_tile(bp, 0);
                 const char* Op = buf_tile(bp, 1);   // dO
+                // transposed operands one step ahead, as above
+                bf16x8 ot[2], qt[2];
+                auto rdt = [&](int n) __attribute__((always_inline)) {
+                    ot[n & 1] = TT::trop(Op, lane, n % NDB, n / NDB);
+                    qt[n & 1] = TT::trop(Qp, lane, n % NDB, n / NDB);
+                };
+                rdt(0);
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        dvT[db] = mfma(TT::trop(Op, lane, db, kk), pp[kk], dvT[db]);
-                        dkT[db] = mfma(TT::trop(Qp, lane, db, kk), ps[kk], dkT[db]);
-                    }
+                for (int n = 0; n < 2 * NDB; ++n) {
+                    if (n + 1 < 2 * NDB) rdt(n + 1);
+                    const int db = n % NDB, kk = n / NDB;
+                    dvT[db] = mfma(ot[n & 1], pp[kk], dvT[db]);
+                    dkT[db] = mfma(qt[n & 1], ps[kk], dkT[db]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             // P and dS die before S and dP are born (registers)
             __builtin_amdgcn_sched_barrier(0);
@@ -374,10 +382,25 @@ __global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, Bwd
                 const char* Ot = buf_tile(bh, 1);
                 sa = f32x16{};
                 pa = f32x16{};
+                // operands one k-step ahead of their products (two register
+                // sets), so each product's LDS reads are in flight during
+                // the previous step's products
+                bf16x8 qa[2], oa[2], ka[2], va[2];
+                auto rd = [&](int ks) __attribute__((always_inline)) {
+                    const int sl = ks & 1;
+                    qa[sl] = TT::rowop(Qt, l32, g, ks);
+                    ka[sl] = TT::colop(Kw, l32, g, ks);
+                    oa[sl] = TT::rowop(Ot, l32, g, ks);
+                    va[sl] = TT::colop(Vw, l32, g, ks);
+                };
+                rd(0);
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    sa = mfma(TT::rowop(Qt, l32, g, ks), TT::colop(Kw, l32, g, ks), sa);
-                    pa = mfma(TT::rowop(Ot, l32, g, ks), TT::colop(Vw, l32, g, ks), pa);
+                    if (ks + 1 < KS) rd(ks + 1);
+                    const int sl = ks & 1;
+                    sa = mfma(qa[sl], ka[sl], sa);
+                    pa = mfma(oa[sl], va[sl], pa);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             // this wave's loads (issued in its last X half-slot) land before
