@@ -569,7 +569,7 @@ def main():
         log("main workload", w.name)
         want_host = not args.no_cpu_baseline
         main_res, host = bench_chunked(torch, swa, w, args.steps, args.warmup, settle, keep_host=want_host)
-        rooflines[w.name] = mfma_roofline("prefill_pp_kernel<128>", "prefill_pp_kernel", w.name,
+        rooflines[w.name] = mfma_roofline("prefill_pp_kernel<128, false>", "prefill_pp_kernel", w.name,
                                           main_res["chunk_flops"], main_res["attn_launch_ms"])
         log("main", main_res)
         torch.cuda.empty_cache()
@@ -577,7 +577,7 @@ def main():
         if wid in todo:
             wk = si.WORKLOADS[wid]
             rk = bench_prefill(torch, swa, wk, max(10, args.steps), 3, settle)
-            rooflines[wk.name] = mfma_roofline("prefill_pp_kernel<128>", "prefill_pp_kernel", wk.name,
+            rooflines[wk.name] = mfma_roofline("prefill_pp_kernel<128, false>", "prefill_pp_kernel", wk.name,
                                                rk["flops"], rk["ms"])
             log("w%d" % wid, rk)
             torch.cuda.empty_cache()
@@ -585,7 +585,7 @@ def main():
         w4 = si.WORKLOADS[4]
         r4 = bench_decode(torch, swa, w4, args.decode_steps, settle)
         dec_gbs = r4["decode_kernel_bytes"] / r4["decode_ms"] / 1e6
-        rooflines[w4.name] = {"bound": "hbm", "kernel": "decode_split_kernel<128,false>", "achieved": dec_gbs,
+        rooflines[w4.name] = {"bound": "hbm", "kernel": "decode_split_kernel<128, false, false>", "achieved": dec_gbs,
                               "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dec_gbs / PEAK_HBM_GBS,
                               "bytes_per_launch": r4["decode_kernel_bytes"], "launch_ms": r4["decode_ms"],
                               "traffic": recorded("decode_split_kernel", w4.name, "traffic",
