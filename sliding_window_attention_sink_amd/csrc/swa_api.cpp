@@ -284,8 +284,9 @@ int swa_rope_keys(const swa_desc* desc, const void* k, int64_t n, int64_t pos0, 
 
 namespace {
 
-// Workspace of swa_prefill_global: gathered global keys and values, the
-// banded rows' log-sum-exp, and the split partials of the dense global rows.
+// Workspace of swa_prefill_global: gathered global keys and values, each
+// position's count of globals below its window, and the split partials of
+// the dense global rows.
 struct GlobalLayout {
     swa_desc dense{};
     int32_t n_split = 1;
