@@ -15,7 +15,10 @@ hand-picked case names.  Three kinds of case:
   definition over the whole history;
 * dilated: the dilated-window prefill;
 * backward (own draws): dq, dk, dv against the oracle's gradients, the
-  forward's bf16 output as o.
+  forward's bf16 output as o;
+* global tokens (own draws): every row of the global-token prefill, with up
+  to 64 globals anywhere in the sequence (among the sinks, inside or past
+  the window).
 
 Large forward cases compare a random sample of rows (first and last rows
 always in).
@@ -223,3 +226,60 @@ def test_backward_sweep_matches_oracle(gpu, c):
     refs = oracle.backward(q, k, v, o, do, s, r)
     for name, got, ref, bar in zip(("dq", "dk", "dv"), (dq, dk, dv), refs, bwd_bounds.bars(q, k, v, o, do, s, r)):
         bwd_bounds.check(name, host(got), ref, bar)
+
+
+# ---- task-bound global tokens: their own seeded draws (bf16)
+N_GLB = 24
+
+
+def glb_case(i: int) -> dict:
+    g = np.random.default_rng(np.random.SeedSequence([0x610B, i]))
+    Hkv = int(g.choice([1, 2, 4]))
+    grp = int(g.choice([1, 2, 4, 8, 16]))
+    while Hkv * grp > 16:
+        grp //= 2
+    L = int(g.choice([int(g.integers(1, 64)), int(g.integers(64, 700)), int(g.integers(700, 1500))],
+                     p=[0.15, 0.45, 0.4]))
+    c = dict(i=i, kind="global", dtype="bf16", B=int(g.choice([1, 2])), Hq=Hkv * grp, Hkv=Hkv,
+             d=int(g.choice([64, 128])), L=L,
+             s=int(g.choice([0, 1, 4, int(g.integers(2, 40)), int(g.integers(40, 140))], p=[0.25, 0.1, 0.3, 0.2, 0.15])),
+             r=int(g.choice([1, int(g.integers(2, 70)), int(g.integers(70, 400)), 4096], p=[0.1, 0.4, 0.35, 0.15])))
+    ng = int(min(L, g.choice([1, int(g.integers(2, 9)), int(g.integers(9, 40)), 64], p=[0.2, 0.4, 0.3, 0.1])))
+    c["globals"] = sorted(int(x) for x in g.choice(L, size=ng, replace=False))
+    return c
+
+
+GLB_CASES = [glb_case(i) for i in range(N_GLB)]
+
+
+def glb_id(c):
+    return "%02d_B%dH%d-%dd%d_L%d_s%d_r%d_ng%d" % (c["i"], c["B"], c["Hq"], c["Hkv"], c["d"], c["L"], c["s"], c["r"],
+                                                  len(c["globals"]))
+
+
+def test_global_sweep_cases_cover_the_paths():
+    """Globals among the sinks and past the window, 64 globals (one full
+    key tile), 16 q-heads per kv-head (one dense row a launch), both head
+    dims (CPU)."""
+    assert any(c["globals"][0] < c["s"] for c in GLB_CASES)
+    assert any(c["globals"][-1] >= c["s"] + c["r"] for c in GLB_CASES)
+    assert any(len(c["globals"]) == 64 for c in GLB_CASES)
+    assert any(c["Hq"] // c["Hkv"] == 16 for c in GLB_CASES)
+    assert {64, 128} <= {c["d"] for c in GLB_CASES}
+    for c in GLB_CASES:
+        assert len(set(c["globals"])) == len(c["globals"]) and max(c["globals"]) < c["L"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("c", GLB_CASES, ids=[glb_id(c) for c in GLB_CASES])
+def test_global_sweep_matches_oracle(gpu, c):
+    import sliding_window_attention_sink_amd as swa
+    say("global sweep", glb_id(c))
+    B, Hq, Hkv, d, L, s, r = c["B"], c["Hq"], c["Hkv"], c["d"], c["L"], c["s"], c["r"]
+    g = np.random.default_rng(np.random.SeedSequence([0x610B, c["i"], 1]))
+    q, k, v = (si.round_bf16(g.standard_normal((B, H, L, d)).astype(np.float32)) for H in (Hq, Hkv, Hkv))
+    o = host(swa.prefill_global(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), s, r, c["globals"]))
+    torch.cuda.synchronize()
+    ref = oracle.prefill_rows(q, k, v, s, r, globals_=c["globals"]).reshape(o.shape)
+    err = max_err(o, ref)
+    assert err <= TOL["bf16"], f"max-abs error {err}"
