@@ -55,11 +55,19 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """A source's code with comments and blank space removed, so a note
+    stays valid across edits of the comments alone."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_sources_sha256(family: str = "prefill_pp_kernel") -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -34,6 +34,12 @@
 // lane's weights of the tile sum past 2^8 (or a row has no max yet) is the
 // exact row max taken and the running state rescaled (exact either way: the
 // same max scales the numerator and the denominator).
+//
+// The call's own rows are addressed through element strides, so a residue
+// class of the dilated window (rows dil apart, the sinks as cache slots) runs
+// in place.  The GLB instantiation adds, after the band and outside the
+// ping-pong, one tile of gathered task-bound global keys (the Longformer
+// section and the glossary entry on global tokens of the t6page page).
 #include <type_traits>
 
 #include "prefill_common.h"
