@@ -630,8 +630,10 @@ def main():
         torch.cuda.empty_cache()
     if 7 in todo:
         extra["dilated_" + w2.name] = bench_dilated(torch, swa, w2, [2, 4], settle=settle)
+        log("dilated", w2.name, extra["dilated_" + w2.name])
         w3 = si.WORKLOADS[3]
         extra["dilated_" + w3.name] = bench_dilated(torch, swa, w3, [2, 8], settle=settle)
+        log("dilated", w3.name, extra["dilated_" + w3.name])
         torch.cuda.empty_cache()
     if 8 in todo:
         w4 = si.WORKLOADS[4]

@@ -99,3 +99,12 @@ def test_global_key_count_sum_is_the_sum_of_key_set_sizes():
     for L, s, r, G in [(300, 4, 28, [2, 50, 51, 299]), (200, 0, 16, [0, 7, 100]), (90, 70, 10, [3, 80])]:
         want = sum(len(oracle.key_set(t, s, r, globals_=G)) for t in range(L))
         assert bench.global_key_count_sum(L, s, r, G) == want
+
+
+def test_note_hash_ignores_comments_only():
+    """A counter note stays valid across comment edits, not across code edits."""
+    a = "int f(int x) { // the row\n  return x + 1; /* next\n tile */ }\n"
+    b = "int f(int x) {\n  // another comment\n  return x + 1;   }\n"
+    c = "int f(int x) { return x + 2; }\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
