@@ -489,15 +489,16 @@ __global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, Bwd
     }
 }
 
-// Adds the partial sums of segments 1 .. of every split key tile to dK and
-// dV, in segment order.  Thread: 4 values of one key.
+// Adds the partial sums of segments 1 .. of every split key tile among keys
+// key0 .. key0+nkeys-1 (of each (batch, kv-head)) to dK and dV, in segment
+// order.  Thread: 4 values of one key.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardArgs a, BwdGrid gr) {
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BackwardArgs a, BwdGrid gr, int key0, int nkeys) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t per_bh = a.L * (D / 4);
+    const int64_t per_bh = (int64_t)nkeys * (D / 4);
     if (idx >= (int64_t)gr.bhkv * per_bh) return;
     const int bhk = (int)(idx / per_bh);
-    const int key = (int)((idx % per_bh) / (D / 4));
+    const int key = key0 + (int)((idx % per_bh) / (D / 4));
     const int e4 = (int)(idx % (D / 4)) * 4;
     const int L = (int)a.L;
     const int tile = key / 128, i0 = tile * 128;
@@ -530,10 +531,22 @@ hipError_t launch(const BackwardArgs& a, const BwdGrid& gr, hipStream_t st) {
     const int64_t items = (int64_t)gr.bhkv * (gr.tiles_sink * gr.nseg_sink + (gr.tiles - gr.tiles_sink) * gr.nseg_band);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)items), dim3(2 * NT), 0, st, a, gr);
     e = hipGetLastError();
-    if (e != hipSuccess || gr.slots_band + gr.slots_sink == 0) return e;
-    const int64_t n = (int64_t)gr.bhkv * a.L * (D / 4);
-    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, gr);
-    return hipGetLastError();
+    if (e != hipSuccess) return e;
+    // only the key tiles that have partial sums: the sink tiles, the band
+    // tiles, or both
+    const int ksink = (int)((int64_t)gr.tiles_sink * 128 < a.L ? (int64_t)gr.tiles_sink * 128 : a.L);
+    if (gr.slots_sink > 0) {
+        const int64_t n = (int64_t)gr.bhkv * ksink * (D / 4);
+        hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, gr, 0, ksink);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (gr.slots_band > 0) {
+        const int nk = (int)(a.L - ksink);
+        const int64_t n = (int64_t)gr.bhkv * nk * (D / 4);
+        hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a, gr, ksink, nk);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace
