@@ -160,7 +160,7 @@ int swa_prefill_dilated(const swa_desc* desc, int32_t dilation, const void* q, c
  * outside its key set), then computes the global rows as dense causal rows,
  * 16 / (Hq/Hkv) of them per decode launch.  Workspace:
  * swa_prefill_global_workspace_bytes(desc, L, ng) bytes (the gathered keys
- * and values, the dense rows' split partials).
+ * and values, one byte per position, the dense rows' split partials).
  * Errors: those of swa_prefill, SWA_ERR_INVALID_ARG for bad globals or a
  * short workspace, SWA_ERR_UNSUPPORTED for fp32, RoPE or wide GQA groups.
  */
