@@ -329,8 +329,9 @@ def global_key_count_sum(L: int, s: int, r: int, G) -> int:
 
 def bench_global(torch, swa, w, G, steps=10, settle=_no_settle):
     """Prefill with task-bound global tokens at positions G on a prefill
-    workload's tensors: the banded pass, the merge of each row's global keys
-    and the dense global rows; algorithmic TFLOP/s of the key sets."""
+    workload's tensors: the gather of the global keys, the banded pass with
+    them as one more key tile, and the dense global rows; algorithmic TFLOP/s
+    of the key sets."""
     q, k, v = __import__("swa_inputs").prefill_inputs(w)
     qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
     del q, k, v

@@ -25,8 +25,8 @@ namespace {
 
 using namespace mt;
 
-// Keys and values of the global positions into [B*Hkv, kMaxGlobals, d]
-// (rows past ng zero).  Thread: one 16-byte chunk.
+// Keys and values of the global positions at or past the sinks into
+// [B*Hkv, kMaxGlobals, d] (rows past ng zero).  Thread: one 16-byte chunk.
 template <int D>
 __global__ __launch_bounds__(256) void global_gather_kernel(GlobalArgs a) {
     constexpr int CH = D / 8;
@@ -47,8 +47,9 @@ __global__ __launch_bounds__(256) void global_gather_kernel(GlobalArgs a) {
     *(u32x4*)((__bf16*)a.vg + dst) = vx;
 }
 
-// gjb[t] = #{j : pos[j] < t - r + 1}: the globals below row t's window (the
-// prefill keeps globals ng_lo .. gjb[t]-1 for row t).  Thread: one row.
+// gjb[t] = #{j : pos[j] < t - r + 1}: the gathered globals (all at or past
+// the sinks) below row t's window; the prefill keeps block rows
+// 0 .. gjb[t]-1 for row t.  Thread: one row.
 __global__ __launch_bounds__(256) void global_rows_kernel(GlobalArgs a) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= a.L) return;
