@@ -243,8 +243,9 @@ int swa_decode_step_noalloc(const swa_desc* desc, const void* q, const void* k_n
  * [B, Hkv, L, d].  Outputs fp32, caller-owned, fully overwritten: dq
  * [B, Hq, L, d]; dk, dv [B, Hkv, L, d].  Workspace: at least
  * swa_backward_workspace_bytes() bytes (per-row log-sum-exp and
- * dout . o), 16-byte aligned.  Sink keys' gradients are accumulated with
- * fp32 atomics, so their rounding order may differ from call to call.
+ * dout . o, then partial dK and dV sums of the key tiles whose queries are
+ * split into segments), 16-byte aligned.  No atomics: the partial sums are
+ * added in a fixed order, so repeated calls give identical gradients.
  * Errors: SWA_ERR_INVALID_ARG (null or misaligned pointer, L < 1, short
  * workspace, shape fields), SWA_ERR_UNSUPPORTED (d, fp32 inputs, RoPE),
  * SWA_ERR_HIP.
