@@ -576,10 +576,20 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // rotated copy is made when the phase changes, from a fresh read of the
     // row (waited for here so no later instruction waits on it), or from the
     // row the prologue read (q_raw: which copy it is meant for).
+    //   With one sink tile and every row of the workgroup at or past s+r-1,
+    // the sink phase's query position is s+r-1 for all rows, and
+    // (R(s+r-1) q) . k = q . (R(-(s+r-1)) k): the sink keys are turned by
+    // -(s+r-1) once in LDS (turn_sinks, below), the sink tile is scored with
+    // the unrotated query, and the band's copy is the same registers rotated
+    // to t, with no second read of the row.
     const bool rope = a.rope_rr > 0.0;
+    const bool sink_turn = rope && nph == 2 && ph0.use_qs && ph0.last == 0 && t0 >= s + r - 1;
     auto ensure_q = [&](int v) __attribute__((always_inline)) {
         const int want_q = (rope && phase_of(v).use_qs) ? 1 : 0;
-        if (want_q != q_loaded) {
+        if (want_q != q_loaded && sink_turn) {
+            if (want_q == 0) T::rope_q(qr, my_t, a.rope_rr, g);
+            q_loaded = want_q;
+        } else if (want_q != q_loaded) {
             if (q_raw != want_q) {
                 T::load_q(qr, (const __bf16*)a.q + qoff, my_valid, g);
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -723,6 +733,27 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     }
     wait_vm(0);
     wg_barrier();
+    if (sink_turn) {
+        // one wave turns the s sink rows of tile 0 (set 0) by -(s+r-1); a
+        // lane takes one chunk pair (dims 8 cp .. and their partners d/2
+        // further) of one key, at the key's place in the K tile layout
+        if (wave == 0) {
+            constexpr int NPAIR = T::CH / 2;
+            char* kt = (char*)smem[0].k;
+            for (int u = lane; u < s * NPAIR; u += 64) {
+                const int j = u / NPAIR, cp = u % NPAIR;
+                const int rho = T::krow(j), blk = rho / T::RPB;
+                char* rowb = kt + blk * 1024 + (rho % T::RPB) * 16;
+                u32x4* lo = (u32x4*)(rowb + (cp ^ T::ksw(blk)) * 16 * T::RPB);
+                u32x4* hi = (u32x4*)(rowb + ((cp + NPAIR) ^ T::ksw(blk)) * 16 * T::RPB);
+                u32x4 x0 = *lo, x1 = *hi;
+                rope::rot_chunk_pair(x0, x1, 8 * cp, -(double)(s + r - 1), a.rope_rr);
+                *lo = x0;
+                *hi = x1;
+            }
+        }
+        __syncthreads();
+    }
     auto end_half = [&]() __attribute__((always_inline)) {
         wait_vm(n_last);
         wg_barrier();
