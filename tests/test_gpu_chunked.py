@@ -74,6 +74,27 @@ def test_chunked_long_window_cache_tiles(gpu, rope_base, Hq, Hkv, chunk):
     assert err <= TOL["bf16"], f"max-abs error {err}"
 
 
+@pytest.mark.parametrize("s,r,d,Hq,Hkv,chunk", [
+    (64, 40, 128, 4, 2, 96),     # one full sink tile, the largest s that turns; GQA pairs
+    (65, 40, 128, 2, 2, 96),     # two sink tiles: the band re-reads its queries; MHA halves
+    (1, 70, 64, 2, 2, 128),      # one sink, d = 64, MHA
+    (4, 60, 64, 8, 2, 200),      # four q-heads per kv-head, d = 64, items straddling s+r-1
+])
+def test_rope_sink_turn_boundaries(gpu, s, r, d, Hq, Hkv, chunk):
+    """RoPE with one sink tile and every row of a work item at or past s+r-1:
+    the sink keys are turned by -(s+r-1) in LDS and scored with the query as
+    read, the band takes the query rotated to t.  Around it: two sink tiles
+    (s = 65), items whose rows straddle s+r-1 (both keep the second read of
+    the queries), d = 64, GQA pairs and MHA halves."""
+    B, L = 1, 700
+    q, k, v = seq_inputs(14, B, Hq, Hkv, L, d)
+    say("rope sink turn", s, r, d, Hq, Hkv, chunk)
+    o = host(run_chunked(q, k, v, s, r, chunk, 10000.0))
+    ref = oracle.chunked_rows(q, k, v, s, r, rope_base=10000.0, rows=None).reshape(o.shape)
+    err = max_err(o, ref)
+    assert err <= TOL["bf16"], f"max-abs error {err}"
+
+
 def test_single_chunk_rope_equals_plain_rope_prefill(gpu):
     """One chunk holding the whole sequence: the RoPE path without a cache."""
     import sliding_window_attention_sink_amd as swa
