@@ -579,7 +579,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     //   With one sink tile and every row of the workgroup at or past s+r-1,
     // the sink phase's query position is s+r-1 for all rows, and
     // (R(s+r-1) q) . k = q . (R(-(s+r-1)) k): the sink keys are turned by
-    // -(s+r-1) once in LDS (turn_sinks, below), the sink tile is scored with
+    // -(s+r-1) once in LDS (after the prologue's loads), the sink tile is scored with
     // the unrotated query, and the band's copy is the same registers rotated
     // to t, with no second read of the row.
     const bool rope = a.rope_rr > 0.0;
