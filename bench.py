@@ -196,25 +196,40 @@ def bench_prefill(torch, swa, w, steps, warmup, settle=_no_settle):
 
 
 def bench_chunked(torch, swa, w, steps, warmup, settle=_no_settle, keep_host=False):
-    """The main step: 32 chunks, each = key rotation + attention + append.
+    """The main step: 32 chunks, each = key rotation + attention with the
+    append fused in (swa_prefill_append: chunk i reads cache pair i % 2 and
+    writes the cache after it to pair (i + 1) % 2; chunks are 4096 >= r
+    tokens).  Also the same step with the separate append launch.
 
-    Returns the step time, the attention kernel's launch duration on a chunk
-    with a full cache (back-to-back launches of one chunk's swa_prefill, the
-    same inputs each time), and the same for the rotation and append calls."""
+    Returns the step times and the launch durations on a chunk with a full
+    cache (back-to-back launches of one chunk's call, the same inputs each
+    time): the fused attention launch, the plain attention launch, the
+    rotation and the separate append."""
     si = __import__("swa_inputs")
     q, k, v = si.chunk_inputs(w, 0, w.L)
     qd, kd, vd = (to_dev(torch, x, torch.bfloat16) for x in (q, k, v))
     host = (q, k, v) if keep_host else None
     del q, k, v
     C = w.chunk
+    assert C >= w.r, "the fused append needs chunks of at least r tokens"
     chunks = [(p0, min(w.L, p0 + C)) for p0 in range(0, w.L, C)]
     parts = [tuple(x[:, :, a:b].contiguous() for x in (qd, kd, vd)) for a, b in chunks]
     del qd, kd, vd
     krot = torch.empty_like(parts[0][1])
     out = torch.empty_like(parts[0][0])
     base = w.rope_base
+    pairs = [swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda") for _ in range(2)]
 
-    def run_chunk(kc, vc, i):
+    def run_chunk(i):
+        (a, b), (qc, kk, vv) = chunks[i], parts[i]
+        kr = krot[:, :, :b - a]
+        kc, vc = pairs[i % 2]
+        kx, vx = pairs[(i + 1) % 2]
+        swa.rope_keys(kk, a, base, out=kr)
+        swa.prefill_append(qc, kr, vv, w.s, w.r, kx, vx, rope_base=base, k_cache=kc if a else None,
+                           v_cache=vc if a else None, pos0=a, out=out[:, :, :b - a])
+
+    def run_chunk_separate(kc, vc, i):
         (a, b), (qc, kk, vv) = chunks[i], parts[i]
         kr = krot[:, :, :b - a]
         swa.rope_keys(kk, a, base, out=kr)
@@ -222,45 +237,58 @@ def bench_chunked(torch, swa, w, steps, warmup, settle=_no_settle, keep_host=Fal
                     pos0=a, out=out[:, :, :b - a])
         swa.cache_append(kr, vv, kc, vc, a, w.s, w.r)
 
-    # one cache for every pass: chunk 0 reads none, and each later chunk reads
-    # only slots the earlier chunks of the same pass wrote
-    kc0, vc0 = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda")
-
+    # chunk 0 reads no cache, and each later chunk reads only the pair its
+    # predecessor in the same pass wrote
     def one_pass():
         for i in range(len(chunks)):
-            run_chunk(kc0, vc0, i)
+            run_chunk(i)
+
+    kc0, vc0 = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda")
+
+    def one_pass_separate():
+        for i in range(len(chunks)):
+            run_chunk_separate(kc0, vc0, i)
 
     for _ in range(max(1, warmup)):
         one_pass()
+        one_pass_separate()
     torch.cuda.synchronize()
     settle()
     ms = time_launches(torch, one_pass, steps)
+    settle()
+    ms_sep = time_launches(torch, one_pass_separate, steps)
     flops = chunk_flops(w, 0, w.L)
 
     # each call on its own, on the chunk after a full cache: the cache state
-    # after chunk m-1, then K back-to-back launches of chunk m's calls
+    # after chunk m-1, then back-to-back launches of chunk m's calls
     m = len(chunks) // 2
     kc, vc = swa.new_cache(w.B, w.Hkv, w.d, w.s, w.r, torch.bfloat16, "cuda")
     for i in range(m):
-        run_chunk(kc, vc, i)
+        run_chunk_separate(kc, vc, i)
     (a, b), (qc, kk, vv) = chunks[m], parts[m]
     swa.rope_keys(kk, a, base, out=krot)
+    kx, vx = pairs[0]
     torch.cuda.synchronize()
     settle()
     n = 20
+    # (the fused launches last: the counter notes take the leg's last 20
+    # launches of the attention kernel)
     attn_ms = time_launches(torch, lambda: swa.prefill(qc, krot, vv, w.s, w.r, rope_base=base, k_cache=kc,
                                                        v_cache=vc, pos0=a, out=out), n)
+    fused_ms = time_launches(torch, lambda: swa.prefill_append(qc, krot, vv, w.s, w.r, kx, vx, rope_base=base,
+                                                               k_cache=kc, v_cache=vc, pos0=a, out=out), n)
     rot_ms = time_launches(torch, lambda: swa.rope_keys(kk, a, base, out=krot), n)
     kc2, vc2 = kc.clone(), vc.clone()
     app_ms = time_launches(torch, lambda: swa.cache_append(krot, vv, kc2, vc2, a, w.s, w.r), n)
     del kc2, vc2
     cflops = chunk_flops(w, a, b)
     res = {"ms": ms, "flops": flops, "tflops": flops / ms / 1e9, "chunk_flops": cflops,
-           "attn_launch_ms": attn_ms, "rope_keys_ms": rot_ms, "append_ms": app_ms,
-           "attn_tflops": cflops / attn_ms / 1e9}
-    # share of the step outside attention, from the per-call times
+           "ms_separate_append": ms_sep, "tflops_separate_append": flops / ms_sep / 1e9,
+           "fused_launch_ms": fused_ms, "attn_launch_ms": attn_ms, "rope_keys_ms": rot_ms, "append_ms": app_ms,
+           "fused_tflops": cflops / fused_ms / 1e9, "attn_tflops": cflops / attn_ms / 1e9}
+    # share of the step outside the attention launches, from the per-call times
     c0 = chunk_flops(w, *chunks[0])
-    attn_total = attn_ms * (len(chunks) - 1 + c0 / cflops)
+    attn_total = fused_ms * (len(chunks) - 1 + c0 / cflops)
     res["non_attention_share"] = max(0.0, 1.0 - attn_total / ms)
     return res, host
 
@@ -578,8 +606,10 @@ def main():
         log("main workload", w.name)
         want_host = not args.no_cpu_baseline
         main_res, host = bench_chunked(torch, swa, w, args.steps, args.warmup, settle, keep_host=want_host)
+        # the dominant kernel of the step: the attention launch with the
+        # append fused in
         rooflines[w.name] = mfma_roofline("prefill_pp_kernel<128, false>", "prefill_pp_kernel", w.name,
-                                          main_res["chunk_flops"], main_res["attn_launch_ms"])
+                                          main_res["chunk_flops"], main_res["fused_launch_ms"])
         log("main", main_res)
         torch.cuda.empty_cache()
     for wid in (2, 3):
@@ -670,9 +700,13 @@ def main():
                        "r": w.r, "chunk": w.chunk, "rope_base": w.rope_base, "global_batch": w.B,
                        "seq_len": w.L, "parallelism": "none (1 GPU)"},
             "roofline": rooflines[w.name],
-            "step_breakdown": {"attn_launch_ms": main_res["attn_launch_ms"], "rope_keys_ms": main_res["rope_keys_ms"],
-                               "append_ms": main_res["append_ms"],
-                               "non_attention_share": main_res["non_attention_share"]},
+            "step_breakdown": {"fused_attention_append_launch_ms": main_res["fused_launch_ms"],
+                               "rope_keys_ms": main_res["rope_keys_ms"],
+                               "non_attention_share": main_res["non_attention_share"],
+                               "attention_only_launch_ms": main_res["attn_launch_ms"],
+                               "separate_append_ms": main_res["append_ms"],
+                               "step_ms_with_separate_append": main_res["ms_separate_append"],
+                               "tflops_with_separate_append": main_res["tflops_separate_append"]},
             "rooflines": rooflines,
             "settle_ms": args.settle_ms,
             "extra": extra,

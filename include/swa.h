@@ -127,6 +127,27 @@ int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new,
                      void* k_cache, void* v_cache, void* stream);
 
 /*
+ * One chunk of the streaming prefill with the append fused in: the rows of
+ * swa_prefill over (k_cache, v_cache) + the chunk (chunked prefill on the
+ * t6page page), and, in the same launch, the cache after appending the
+ * chunk (swa_cache_append's result) written to a second cache pair
+ * (k_next, v_next, [B, Hkv, s + r, d]); k_cache / v_cache are only read.
+ * The call needs every rolling slot that holds a token afterwards to come
+ * from the chunk: L >= r, or pos0 <= s.  Then k_next / v_next receive the
+ * chunk's surviving tokens at their slots and the sink slots below pos0
+ * from the cache; slots that hold no token after the call are not written.
+ * Alternating two cache pairs, chunk by chunk, gives the rows and caches of
+ * swa_prefill + swa_cache_append without the separate copy launch.
+ * bf16 only; the cache pairs must not overlap (k_next != k_cache, ...).
+ * Errors: those of swa_prefill, SWA_ERR_INVALID_ARG for L < r with
+ * pos0 > s, a null or misaligned next cache, or next == current,
+ * SWA_ERR_UNSUPPORTED for fp32.
+ */
+int swa_prefill_append(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
+                       const void* k_cache, const void* v_cache, int64_t pos0, void* k_next, void* v_next,
+                       void* stream);
+
+/*
  * Dilated sliding window (prefill, no cache, no RoPE): query t attends the
  * sinks 0 .. min(s, t+1)-1 and the r positions t, t - dilation, ...,
  * t - (r-1) dilation that are >= s (the glossary entry on dilated SWA and

@@ -11,6 +11,9 @@ of include/swa.h); this package binds it for PyTorch callers:
   * prefill_global(q, k, v, s, r, globals) the same with task-bound global
                                        tokens
   * cache_append(k, v, kc, vc, pos0, ...) write tokens into the rolling cache
+  * prefill_append(q, k, v, s, r, kc_next, vc_next, ...) a chunk's rows and
+                                       the cache after it, into a second
+                                       cache pair, in one launch
   * decode(q, kc, vc, T, s, r, ...)    split-K single-query decode
   * decode_step(q, k, v, kc, vc, T, s, r, ...) append token T-1 and decode
                                        it in one launch
@@ -31,6 +34,7 @@ from .ops import (  # noqa: F401
     make_desc,
     new_cache,
     prefill,
+    prefill_append,
     prefill_dilated,
     prefill_global,
     prefill_workspace_bytes,

@@ -21,7 +21,8 @@ SWA_BF16 = 1
 
 # every symbol include/swa.h declares
 EXPORTS = (
-    "swa_prefill_workspace_bytes", "swa_rope_keys", "swa_prefill", "swa_cache_append", "swa_decode_workspace_bytes",
+    "swa_prefill_workspace_bytes", "swa_rope_keys", "swa_prefill", "swa_cache_append", "swa_prefill_append",
+    "swa_decode_workspace_bytes",
     "swa_decode", "swa_decode_step", "swa_decode_step_noalloc", "swa_decode_default_splits", "swa_prefill_dilated_workspace_bytes",
     "swa_prefill_dilated", "swa_prefill_global_workspace_bytes", "swa_prefill_global", "swa_backward_workspace_bytes", "swa_backward", "swa_status_str", "swa_last_error",
     "swa_abi_version",
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.swa_prefill.restype = ctypes.c_int
     lib.swa_cache_append.argtypes = [dp, vp, vp, i64, i64, vp, vp, vp]
     lib.swa_cache_append.restype = ctypes.c_int
+    lib.swa_prefill_append.argtypes = [dp, vp, vp, vp, vp, i64, vp, vp, i64, vp, vp, vp]
+    lib.swa_prefill_append.restype = ctypes.c_int
     lib.swa_decode_workspace_bytes.argtypes = [dp, i32]
     lib.swa_decode_workspace_bytes.restype = sz
     lib.swa_decode.argtypes = [dp, vp, vp, vp, i64, vp, i32, vp, sz, vp]
@@ -118,6 +121,11 @@ def swa_prefill(desc, q, k, v, o, L, k_cache, v_cache, pos0, workspace, workspac
 
 def swa_cache_append(desc, k_new, v_new, n, pos0, k_cache, v_cache, stream) -> int:
     return load().swa_cache_append(ctypes.byref(desc), k_new, v_new, n, pos0, k_cache, v_cache, stream)
+
+
+def swa_prefill_append(desc, q, k, v, o, L, k_cache, v_cache, pos0, k_next, v_next, stream) -> int:
+    return load().swa_prefill_append(ctypes.byref(desc), q, k, v, o, L, k_cache, v_cache, pos0, k_next, v_next,
+                                     stream)
 
 
 def swa_decode_workspace_bytes(desc: SwaDesc, n_split: int) -> int:

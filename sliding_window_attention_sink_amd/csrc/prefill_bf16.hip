@@ -317,10 +317,20 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// What the fused append of a work item needs at its end (see below).
+struct FuseInfo {
+    const __bf16* src[2];      // the item's own K and V rows (row 0 = position pos0)
+    __bf16* dst[2];            // the next cache's K and V of the item's (batch, kv-head)
+    const __bf16* csrc[2];     // the current cache's K and V (sink slots below pos0), or null
+    int64_t keep;              // first position past the sinks that survives the call
+    int32_t write, pz, row0, nrow, s, r;
+};
+
 template <int D, bool GLB>
 __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     typedef PP<D> T;
     __shared__ typename T::Buf smem[NSET];
+    __shared__ FuseInfo finfo;
 
     const int s = a.s, r = a.r;
     const int pos0 = (int)a.pos0;
@@ -754,6 +764,80 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         }
         __syncthreads();
     }
+    // Fused append (kc_next set, plain kernel): the workgroup's own key and
+    // value rows that survive the call (positions from pos0 + L - r on, and
+    // those below s) go to their slots of the next cache; the items of the
+    // kv-head's first q-head (pair, in pair mode) write them (the other
+    // q-heads' items have the same rows).  Group 0 loads the K rows into registers in its
+    // last half-slot, which has no products (group 1 runs its last
+    // cluster), group 1 the V rows after that cluster; both store them
+    // after the output rows.  Every thread of a group issues exactly FN
+    // loads (rows past the item or superseded read the item's first row and
+    // are not stored), after its last tile loads, so the wait below can
+    // leave them in flight.  The item of the first query tile also copies
+    // the sink slots below pos0 from the cache.  What the copy needs is put
+    // in LDS by thread 0 before the first barrier and read back at the end
+    // (held in scalar registers across the band it would crowd them).
+    constexpr int FCH = D / 8;                 // 16-byte chunks per row
+    constexpr int FN = FCH;                    // 256 rows x FCH chunks over a group's 256 threads
+    if constexpr (!GLB) {
+        if (tid == 0) {
+            // one writer per row: the kv-head's first q-head (pair)
+            const bool w = a.kc_next != nullptr && h - kvh * G < (a.pair_mode ? 2 : 1);
+            finfo.write = w ? 1 : 0;
+            if (w) {
+                finfo.src[0] = kn;
+                finfo.src[1] = vn;
+                finfo.dst[0] = (__bf16*)a.kc_next + (size_t)(b * a.Hkv + kvh) * a.c_bh;
+                finfo.dst[1] = (__bf16*)a.vc_next + (size_t)(b * a.Hkv + kvh) * a.c_bh;
+                finfo.csrc[0] = kc;
+                finfo.csrc[1] = vc;
+                finfo.keep = pos0 + a.L - r;
+                finfo.pz = pos0;
+                finfo.row0 = row0;
+                finfo.nrow = nrows;
+                finfo.s = s;
+                finfo.r = r;
+            }
+        }
+    }
+    u32x4 fdat[FN];
+    int fdst[FN];
+    auto fuse_write = [&]() __attribute__((always_inline)) -> bool {
+        if constexpr (GLB) return false;
+        return __builtin_amdgcn_readfirstlane(finfo.write) != 0;
+    };
+    auto fuse_load = [&]() __attribute__((always_inline)) {
+        const __bf16* src = finfo.src[grp];       // group 0 the keys, group 1 the values (dense: row i at i d)
+        const int sz = finfo.s, rz = finfo.r, pz = finfo.pz, row0f = finfo.row0, nrow = finfo.nrow;
+        const int64_t keep = finfo.keep;
+        const int gt = tid & 255;
+#pragma unroll
+        for (int k = 0; k < FN; ++k) {
+            const int f = gt + k * 256;                         // (row, chunk)
+            const int ch = f % FCH, i = f / FCH;
+            const int p = pz + row0f + i;
+            const bool live = i < nrow && (p < sz || p >= keep);
+            fdst[k] = live ? (p < sz ? p : sz + p % rz) * D + 8 * ch : -1;
+            fdat[k] = *(const u32x4*)(src + (size_t)(row0f + (live ? i : 0)) * D + 8 * ch);
+        }
+    };
+    auto fuse_store = [&]() __attribute__((always_inline)) {
+        __bf16* dst = finfo.dst[grp];
+#pragma unroll
+        for (int k = 0; k < FN; ++k)
+            if (fdst[k] >= 0) *(u32x4*)(dst + fdst[k]) = fdat[k];
+        // the sink slots below pos0 come from the cache
+        const __bf16* cs = finfo.csrc[grp];
+        if (finfo.row0 == 0 && cs != nullptr) {
+            const int ns = finfo.s < finfo.pz ? finfo.s : finfo.pz;
+            for (int u = tid & 255; u < ns * FCH; u += 256) {
+                const int j = u / FCH, ch = u % FCH;
+                *(u32x4*)(dst + j * D + 8 * ch) = *(const u32x4*)(cs + j * D + 8 * ch);
+            }
+        }
+    };
+
     auto end_half = [&]() __attribute__((always_inline)) {
         wait_vm(n_last);
         wg_barrier();
@@ -813,6 +897,10 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
             n_last = 0;
             c_last(set);
             end_half();
+            if (fuse_write()) {
+                fuse_load();
+                n_last = FN;
+            }
             end_half();
         } else {
             x_half(K_, -1, 0, 2);
@@ -832,6 +920,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
             end_half();
             c_last(set);
             end_half();
+            if (fuse_write()) fuse_load();
         }
     }
 
@@ -877,17 +966,25 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         }
     }
 
-    // the buffers take the output rows once every load has landed and every
-    // wave is past its last read
-    wait_vm(0);
+    // the buffers take the output rows once every tile load has landed and
+    // every wave is past its last read (a fused append's FN loads, issued
+    // after each wave's tile loads, stay in flight)
+    const bool fw = fuse_write();
+    if (fw) {
+        if (FN == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+        wait_vm(0);
+    }
     wg_barrier();
-    if (!wave_active) return;
-    const float l_tot = l_part + __shfl_xor(l_part, 32);
-    static_assert(PW * WROWS * T::ORS <= (int)sizeof(smem), "output staging fits the tile buffers");
-    T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * rs, rsb, oacc,
-               my_valid ? 1.0f / l_tot : 0.0f, lane, tw1 - tw0 + 1);
+    if (wave_active) {
+        const float l_tot = l_part + __shfl_xor(l_part, 32);
+        static_assert(PW * WROWS * T::ORS <= (int)sizeof(smem), "output staging fits the tile buffers");
+        T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * rs, rsb, oacc,
+                   my_valid ? 1.0f / l_tot : 0.0f, lane, tw1 - tw0 + 1);
+    }
+    if (fw) fuse_store();
 }
-
 template <int D>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
     const long long G = a.Hq / a.Hkv;

@@ -184,8 +184,10 @@ hipError_t launch_prefill(const swa_desc* desc, const swa::PrefillArgs& a, hipSt
 }
 
 // swa_prefill
+// swa_prefill, and with k_next / v_next swa_prefill_append
 int prefill_impl(const char* fn, const swa_desc* desc, const void* q, const void* k, const void* v, void* o,
-                 int64_t L, const void* k_cache, const void* v_cache, int64_t pos0, void* stream) {
+                 int64_t L, const void* k_cache, const void* v_cache, int64_t pos0, void* stream,
+                 void* k_next = nullptr, void* v_next = nullptr, bool fused = false) {
     clear_error();
     int st = check_desc(desc, fn);
     if (st) return st;
@@ -204,9 +206,21 @@ int prefill_impl(const char* fn, const swa_desc* desc, const void* q, const void
     const bool rope = desc->rope_base > 0.0f;
     if ((int64_t)desc->B * desc->Hq * prefill_mtiles(desc, L) > 0x7fffffffLL)
         return fail(SWA_ERR_INVALID_ARG, "%s: grid too large", fn);
+    if (fused) {
+        if (desc->dtype != SWA_BF16) return fail(SWA_ERR_UNSUPPORTED, "%s: the fused append is built for bf16", fn);
+        if ((st = check_ptr(k_next, fn, "k_next")) || (st = check_ptr(v_next, fn, "v_next"))) return st;
+        if (k_next == k_cache || v_next == v_cache || k_next == v_next || k_next == v_cache || v_next == k_cache)
+            return fail(SWA_ERR_INVALID_ARG, "%s: the next cache must be another buffer pair", fn);
+        // every rolling slot that holds a token afterwards comes from the chunk
+        if (L < desc->r && pos0 > desc->s)
+            return fail(SWA_ERR_INVALID_ARG, "%s: needs L >= r or pos0 <= s (L %lld, r %d, pos0 %lld, s %d)", fn,
+                        (long long)L, desc->r, (long long)pos0, desc->s);
+    }
 
     swa::PrefillArgs a = dense_prefill_args(desc, q, k, v, o, L, has_cache ? k_cache : nullptr,
                                             has_cache ? v_cache : nullptr, pos0);
+    a.kc_next = k_next;
+    a.vc_next = v_next;
     if (rope) {
         // the keys (own and cached) come rotated; the kernel turns the queries
         a.merge_sink = 0;
@@ -225,6 +239,13 @@ int swa_prefill(const swa_desc* desc, const void* q, const void* k, const void* 
     (void)workspace;         // no prefill kernel uses one (swa_prefill_workspace_bytes is 0)
     (void)workspace_bytes;
     return prefill_impl("swa_prefill", desc, q, k, v, o, L, k_cache, v_cache, pos0, stream);
+}
+
+int swa_prefill_append(const swa_desc* desc, const void* q, const void* k, const void* v, void* o, int64_t L,
+                       const void* k_cache, const void* v_cache, int64_t pos0, void* k_next, void* v_next,
+                       void* stream) {
+    return prefill_impl("swa_prefill_append", desc, q, k, v, o, L, k_cache, v_cache, pos0, stream, k_next, v_next,
+                        true);
 }
 
 int swa_cache_append(const swa_desc* desc, const void* k_new, const void* v_new, int64_t n, int64_t pos0,

@@ -53,6 +53,13 @@ struct PrefillArgs {
     // window or in the future).
     const uint8_t* gjb;   // [L]
     int32_t ng;
+    // Fused append (kc_next set; bf16 kernel, dense call, L >= r): the cache
+    // after this call, written to a second cache: the own rows that survive
+    // (positions >= pos0 + L - r, and those below s) at their slots, the
+    // sink slots below pos0 copied from kc / vc.  Every rolling slot is
+    // rewritten (L >= r), so nothing of kc_next is read.
+    void* kc_next;
+    void* vc_next;
 };
 
 struct AppendArgs {

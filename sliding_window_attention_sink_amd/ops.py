@@ -92,6 +92,30 @@ def prefill(q, k, v, s, r, *, scale=None, rope_base=0.0, k_cache=None, v_cache=N
     return out
 
 
+def prefill_append(q, k, v, s, r, k_next, v_next, *, scale=None, rope_base=0.0, k_cache=None, v_cache=None,
+                   pos0=0, out=None, stream=None):
+    """prefill's rows over (k_cache, v_cache) + the chunk, and the cache after
+    appending the chunk written to (k_next, v_next) in the same launch (bf16;
+    needs L >= r or pos0 <= s; the current cache is only read)."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    desc = make_desc(B, Hq, Hkv, d, s, r, q.dtype, scale, rope_base)
+    _need(k, "k", (B, Hkv, L, d), q.dtype, dev)
+    _need(v, "v", (B, Hkv, L, d), q.dtype, dev)
+    if k_cache is not None or v_cache is not None:
+        _need(k_cache, "k_cache", (B, Hkv, s + r, d), q.dtype, dev)
+        _need(v_cache, "v_cache", (B, Hkv, s + r, d), q.dtype, dev)
+    _need(k_next, "k_next", (B, Hkv, s + r, d), q.dtype, dev)
+    _need(v_next, "v_next", (B, Hkv, s + r, d), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.shape, q.dtype, dev)
+    check(_lib.swa_prefill_append(desc, _ptr(q), _ptr(k), _ptr(v), _ptr(out), L, _ptr(k_cache), _ptr(v_cache),
+                                  pos0, _ptr(k_next), _ptr(v_next), _stream(dev, stream)))
+    return out
+
+
 def new_cache(B, Hkv, d, s, r, dtype, device, fill=0.0):
     """Caller-owned rolling cache pair [B, Hkv, s+r, d] (fill e.g. NaN to poison unwritten slots)."""
     kc = torch.full((B, Hkv, s + r, d), fill, dtype=dtype, device=device)

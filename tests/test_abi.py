@@ -109,6 +109,23 @@ def test_rope_decode_group_limit():
     assert "8 q-heads" in _lib.swa_last_error()
 
 
+def test_prefill_append_rejects():
+    d_ = desc()          # s = 4, r = 28
+    G, H = 0x90000, 0xA0000
+    call = lambda dd, L=40, kc=E, vc=F, pos0=64, kn=G, vn=H: _lib.swa_prefill_append(
+        dd, A, B_, C, D, L, kc, vc, pos0, kn, vn, None)
+    assert call(d_, kn=None) == -1 and "k_next is NULL" in _lib.swa_last_error()
+    assert call(d_, vn=H + 8) == -1 and "aligned" in _lib.swa_last_error()
+    assert call(d_, kn=E) == -1 and "another buffer" in _lib.swa_last_error()
+    assert call(d_, vn=G) == -1 and "another buffer" in _lib.swa_last_error()
+    # a chunk shorter than r past the sinks leaves cached tokens in rolling slots
+    assert call(d_, L=27) == -1 and "L >= r or pos0 <= s" in _lib.swa_last_error()
+    assert call(desc(dtype=_lib.SWA_F32)) == -2 and "bf16" in _lib.swa_last_error()
+    # the checks of swa_prefill come first
+    assert call(d_, L=0) == -1 and "L must be" in _lib.swa_last_error()
+    assert call(d_, kc=None, vc=None) == -1 and "cache" in _lib.swa_last_error()
+
+
 def test_append_rejects():
     d_ = desc()
     assert _lib.swa_cache_append(d_, A, B_, 0, 0, C, D, None) == -1 and "n must be" in _lib.swa_last_error()
