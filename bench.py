@@ -608,7 +608,7 @@ def main():
         main_res, host = bench_chunked(torch, swa, w, args.steps, args.warmup, settle, keep_host=want_host)
         # the dominant kernel of the step: the attention launch with the
         # append fused in
-        rooflines[w.name] = mfma_roofline("prefill_pp_kernel<128, false>", "prefill_pp_kernel", w.name,
+        rooflines[w.name] = mfma_roofline("prefill_pp_kernel<128, false, true>", "prefill_pp_kernel", w.name,
                                           main_res["chunk_flops"], main_res["fused_launch_ms"])
         log("main", main_res)
         torch.cuda.empty_cache()
@@ -616,7 +616,7 @@ def main():
         if wid in todo:
             wk = si.WORKLOADS[wid]
             rk = bench_prefill(torch, swa, wk, max(10, args.steps), 3, settle)
-            rooflines[wk.name] = mfma_roofline("prefill_pp_kernel<128, false>", "prefill_pp_kernel", wk.name,
+            rooflines[wk.name] = mfma_roofline("prefill_pp_kernel<128, false, false>", "prefill_pp_kernel", wk.name,
                                                rk["flops"], rk["ms"])
             log("w%d" % wid, rk)
             torch.cuda.empty_cache()

@@ -62,7 +62,7 @@ SPILL_OK = {
     # alive through the band's last products, and two values held across the
     # band go to scratch (one reloaded in the masked-tile path); the plain
     # kernel, which every other call runs, has no spill
-    "_ZN3swa12_GLOBAL__N_117prefill_pp_kernelILi128ELb1EEEvNS_11PrefillArgsE",
+    "_ZN3swa12_GLOBAL__N_117prefill_pp_kernelILi128ELb1ELb0EEEvNS_11PrefillArgsE",
 }
 
 

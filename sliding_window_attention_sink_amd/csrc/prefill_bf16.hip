@@ -305,7 +305,9 @@ __device__ __forceinline__ void wait_vm(int n) {
     else if (n == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     else if (n == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
     else if (n == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else if (n == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else if (n == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
 // Workgroup barrier without a memory fence (the direct loads are waited
@@ -317,16 +319,19 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// What the fused append of a work item needs at its end (see below).
+// What the fused append of a work item needs during the band and at its end
+// (see below).
 struct FuseInfo {
-    const __bf16* src[2];      // the item's own K and V rows (row 0 = position pos0)
     __bf16* dst[2];            // the next cache's K and V of the item's (batch, kv-head)
+    const __bf16* src[2];      // the item's own K and V rows (row 0 = position pos0)
     const __bf16* csrc[2];     // the current cache's K and V (sink slots below pos0), or null
-    int64_t keep;              // first position past the sinks that survives the call
-    int32_t write, pz, row0, nrow, s, r;
+    int32_t write;             // this item writes the next cache
+    int32_t keep_lo;           // first surviving position past the sinks
+    int32_t f0, f1;            // the own survivors' full tiles: positions f0 .. f1
+    int32_t pz, row0, s, r;
 };
 
-template <int D, bool GLB>
+template <int D, bool GLB, bool FUSE>
 __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     typedef PP<D> T;
     __shared__ typename T::Buf smem[NSET];
@@ -679,7 +684,11 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
             }
             const bool full = kb + 63 <= tw0 && (kb >= lo_w1 || kb + 63 < P.sink_hi);
             if (!full) {
-                const int lo_me = P.band_lo > my_t - r + 1 ? P.band_lo : my_t - r + 1;
+                // (with the fused append, r through an empty asm: my_t - r +
+                // 1 formed here, not held across the loop)
+                int r_ = r;
+                if constexpr (FUSE) asm volatile("" : "+s"(r_));
+                const int lo_me = P.band_lo > my_t - r_ + 1 ? P.band_lo : my_t - r_ + 1;
                 const int kbg = kb + 8 * g;
                 const int lim_t = my_t - kbg, lim_s = P.sink_hi - kbg, lim_b = lo_me - kbg;
                 // Most cut tiles hold no sinks and cut one edge only: the
@@ -764,76 +773,123 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         }
         __syncthreads();
     }
-    // Fused append (kc_next set, plain kernel): the workgroup's own key and
+    // Fused append (the FUSE instantiation, kc_next set): the workgroup's own key and
     // value rows that survive the call (positions from pos0 + L - r on, and
     // those below s) go to their slots of the next cache; the items of the
     // kv-head's first q-head (pair, in pair mode) write them (the other
-    // q-heads' items have the same rows).  Group 0 loads the K rows into registers in its
-    // last half-slot, which has no products (group 1 runs its last
-    // cluster), group 1 the V rows after that cluster; both store them
-    // after the output rows.  Every thread of a group issues exactly FN
-    // loads (rows past the item or superseded read the item's first row and
-    // are not stored), after its last tile loads, so the wait below can
-    // leave them in flight.  The item of the first query tile also copies
-    // the sink slots below pos0 from the cache.  What the copy needs is put
-    // in LDS by thread 0 before the first barrier and read back at the end
-    // (held in scalar registers across the band it would crowd them).
-    constexpr int FCH = D / 8;                 // 16-byte chunks per row
-    constexpr int FN = FCH;                    // 256 rows x FCH chunks over a group's 256 threads
-    if constexpr (!GLB) {
+    // q-heads' items have the same rows).  Tiles of the band whose 64 rows
+    // are all own rows that survive are copied from LDS while resident:
+    // group 0 takes the K rows of tile v in its X(v) half-slot (K of tile v
+    // sits in set v % 3 through half-slot 2v+1), group 1 the V rows in its
+    // X(v) (V of tile v sits in set (v+1) % 3 from 2v+2 to 2v+4); the wave
+    // issues its NS stores after its tile loads and the half-slot's wait
+    // counts them.  The other surviving rows (a partial tile at either end
+    // of the item, positions below s, and in the item of the first query
+    // tile the cache's sink slots below pos0) are copied from global memory
+    // at the end.  What the copy needs is put in LDS by thread 0 before the
+    // band (held in scalar registers across it, it would crowd them).
+    constexpr int NS = 16 * T::CH / 64;        // stores per lane: 16 rows of a tile per wave
+    if constexpr (FUSE) {
         if (tid == 0) {
             // one writer per row: the kv-head's first q-head (pair)
             const bool w = a.kc_next != nullptr && h - kvh * G < (a.pair_mode ? 2 : 1);
             finfo.write = w ? 1 : 0;
             if (w) {
-                finfo.src[0] = kn;
-                finfo.src[1] = vn;
                 finfo.dst[0] = (__bf16*)a.kc_next + (size_t)(b * a.Hkv + kvh) * a.c_bh;
                 finfo.dst[1] = (__bf16*)a.vc_next + (size_t)(b * a.Hkv + kvh) * a.c_bh;
+                finfo.src[0] = kn;
+                finfo.src[1] = vn;
                 finfo.csrc[0] = kc;
                 finfo.csrc[1] = vc;
-                finfo.keep = pos0 + a.L - r;
+                const int64_t keep = pos0 + a.L - r;
+                const int klo = (int)(keep > s ? keep : s);
+                const int a0 = t0 > klo ? t0 : klo;                // first own survivor past the sinks
+                finfo.keep_lo = klo;
+                finfo.f0 = (a0 + BN - 1) / BN * BN;                 // full tiles: [f0, f1]
+                finfo.f1 = (t1 + 1) / BN * BN - 1;
                 finfo.pz = pos0;
                 finfo.row0 = row0;
-                finfo.nrow = nrows;
                 finfo.s = s;
                 finfo.r = r;
             }
         }
+        // the record is written before the wave's next barrier
+        if (wave == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    u32x4 fdat[FN];
-    int fdst[FN];
-    auto fuse_write = [&]() __attribute__((always_inline)) -> bool {
-        if constexpr (GLB) return false;
-        return __builtin_amdgcn_readfirstlane(finfo.write) != 0;
-    };
-    auto fuse_load = [&]() __attribute__((always_inline)) {
-        const __bf16* src = finfo.src[grp];       // group 0 the keys, group 1 the values (dense: row i at i d)
-        const int sz = finfo.s, rz = finfo.r, pz = finfo.pz, row0f = finfo.row0, nrow = finfo.nrow;
-        const int64_t keep = finfo.keep;
-        const int gt = tid & 255;
+    // X(v)'s copy of tile v (K for group 0, V for group 1) when all its rows
+    // are own survivors of the item
+    auto copy_own = [&](int v, int cset) __attribute__((always_inline)) {
+        if constexpr (FUSE) {
+            const int kb = tile_of(v) * BN;
+            if (kb + BN - 1 > t1 || kb < t0 || v < vo) return;       // not all own rows (or a sink-phase tile)
+            if (__builtin_amdgcn_readfirstlane(finfo.write) == 0) return;
+            if (kb < __builtin_amdgcn_readfirstlane(finfo.f0)) return;
+            const int sz = __builtin_amdgcn_readfirstlane(finfo.s), rz = __builtin_amdgcn_readfirstlane(finfo.r);
+            // the next cache's base as a wave-uniform global pointer; each
+            // half goes through uint32_t (readfirstlane returns int, whose
+            // widening would sign-extend the low half into the high one)
+            typedef __attribute__((address_space(1))) char gchar;
+            typedef __attribute__((address_space(1))) u32x4 gu32x4;
+            const uint64_t dp = (uint64_t)(uintptr_t)finfo.dst[grp];
+            const uint64_t dlo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)dp);
+            const uint64_t dhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(dp >> 32));
+            gchar* dstb = (gchar*)(uintptr_t)((dhi << 32) | dlo) + (size_t)sz * T::RB;
+            const char* tile = grp == 0 ? (const char*)smem[cset].k : (const char*)smem[cset].v;
+            const int rel0 = kb % rz;                                   // slot of row 0 is sz + rel0 (one wrap at most)
 #pragma unroll
-        for (int k = 0; k < FN; ++k) {
-            const int f = gt + k * 256;                         // (row, chunk)
-            const int ch = f % FCH, i = f / FCH;
-            const int p = pz + row0f + i;
-            const bool live = i < nrow && (p < sz || p >= keep);
-            fdst[k] = live ? (p < sz ? p : sz + p % rz) * D + 8 * ch : -1;
-            fdat[k] = *(const u32x4*)(src + (size_t)(row0f + (live ? i : 0)) * D + 8 * ch);
+            for (int it = 0; it < NS; ++it) {
+                const int u = lane + 64 * it, ch = u % T::CH;
+                const int row = 16 * sub + u / T::CH;                   // key kb + row
+                int off;
+                if (grp == 0) {
+                    const int rho = T::krow(row), blk = rho / T::RPB;
+                    off = blk * 1024 + (ch ^ T::ksw(blk)) * 16 * T::RPB + (rho % T::RPB) * 16;
+                } else {
+                    off = row * T::RB + (ch ^ T::vsw(row)) * 16;
+                }
+                const u32x4 x = *(const u32x4*)(tile + off);
+                int rel = rel0 + row;
+                rel = rel >= rz ? rel - rz : rel;
+                // a uniform base and a 32-bit lane offset (one address register)
+                *(gu32x4*)(dstb + (uint32_t)(rel * T::RB + 16 * ch)) = x;
+                // one chunk in registers at a time (the softmax's values are live)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            n_last += NS;
         }
     };
-    auto fuse_store = [&]() __attribute__((always_inline)) {
-        __bf16* dst = finfo.dst[grp];
-#pragma unroll
-        for (int k = 0; k < FN; ++k)
-            if (fdst[k] >= 0) *(u32x4*)(dst + fdst[k]) = fdat[k];
-        // the sink slots below pos0 come from the cache
-        const __bf16* cs = finfo.csrc[grp];
-        if (finfo.row0 == 0 && cs != nullptr) {
-            const int ns = finfo.s < finfo.pz ? finfo.s : finfo.pz;
-            for (int u = tid & 255; u < ns * FCH; u += 256) {
-                const int j = u / FCH, ch = u % FCH;
-                *(u32x4*)(dst + j * D + 8 * ch) = *(const u32x4*)(cs + j * D + 8 * ch);
+    // the rest at the end, from global memory: own survivors outside the
+    // full tiles, own positions below s, the cache's sinks below pos0
+    auto fuse_tail = [&]() __attribute__((always_inline)) {
+        if constexpr (FUSE) {
+            if (__builtin_amdgcn_readfirstlane(finfo.write) == 0) return;
+            const int sz = finfo.s, rz = finfo.r, pz = finfo.pz, row0f = finfo.row0;
+            const int t0f = pz + row0f, t1f = t1;
+            const int a0 = t0f > finfo.keep_lo ? t0f : finfo.keep_lo, f0 = finfo.f0, f1 = finfo.f1;
+            __bf16* dst = finfo.dst[grp];
+            const __bf16* src = finfo.src[grp];
+            const int gt = tid & 255;
+            auto rows = [&](int p0, int p1, bool sink) __attribute__((always_inline)) {
+                for (int u = gt; u < (p1 - p0 + 1) * T::CH; u += 256) {
+                    const int p = p0 + u / T::CH, ch = u % T::CH;
+                    const int slot = sink ? p : sz + p % rz;
+                    *(u32x4*)(dst + (size_t)slot * D + 8 * ch) = *(const u32x4*)(src + (size_t)(p - pz) * D + 8 * ch);
+                }
+            };
+            if (f0 > f1) {
+                rows(a0, t1f, false);                                   // no full tile
+            } else {
+                rows(a0, f0 - 1, false);
+                rows(f1 + 1, t1f, false);
+            }
+            if (t0f < sz) rows(t0f, (sz - 1) < t1f ? sz - 1 : t1f, true);
+            const __bf16* cs = finfo.csrc[grp];
+            if (row0f == 0 && cs != nullptr) {
+                const int ns = sz < pz ? sz : pz;
+                for (int u = gt; u < ns * T::CH; u += 256) {
+                    const int j = u / T::CH, ch = u % T::CH;
+                    *(u32x4*)(dst + j * D + 8 * ch) = *(const u32x4*)(cs + j * D + 8 * ch);
+                }
             }
         }
     };
@@ -845,10 +901,11 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // this group's X half-slot: its loads (group 1 at hs = 2v: K of tile
     // v+2; group 0 at hs = 2v+1: V of tile v+1; both into set (v+2) % 3),
     // then the softmax of tile vx
-    auto x_half = [&](auto is_k_c, int vx, int v, int nset) __attribute__((always_inline)) {
+    auto x_half = [&](auto is_k_c, int vx, int v, int nset, int cset) __attribute__((always_inline)) {
         n_last = T::JN;
         issue_run(is_k_c, decltype(is_k_c)::value ? v + 2 : v + 1, nset);
         if (wave_active && vx >= 0) cluster_x(vx);
+        if (FUSE && vx >= 0) copy_own(vx, cset);
     };
 
     // Whether some row of this wave has a key of tile v in its key set.  The
@@ -883,44 +940,39 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         if (grp == 0) {
             c_first();
             end_half();
-            x_half(V_, 0, 0, 2);
+            x_half(V_, 0, 0, 2, 0);
             end_half();
             int set = 1;                       // v % 3
             for (int v = 1; v < nv; ++v) {
                 const int nset = set == 0 ? 2 : set - 1;   // (v + 2) % 3
                 c_mid(v, set);
                 end_half();
-                x_half(V_, v, v, nset);
+                x_half(V_, v, v, nset, set);
                 end_half();
                 set = set == 2 ? 0 : set + 1;
             }
             n_last = 0;
             c_last(set);
             end_half();
-            if (fuse_write()) {
-                fuse_load();
-                n_last = FN;
-            }
             end_half();
         } else {
-            x_half(K_, -1, 0, 2);
+            x_half(K_, -1, 0, 2, 0);
             end_half();
             c_first();
             end_half();
             int set = 1;
             for (int v = 1; v < nv; ++v) {
                 const int nset = set == 0 ? 2 : set - 1;
-                x_half(K_, v - 1, v, nset);
+                x_half(K_, v - 1, v, nset, set);
                 end_half();
                 c_mid(v, set);
                 end_half();
                 set = set == 2 ? 0 : set + 1;
             }
-            x_half(K_, nv - 1, nv, set == 0 ? 2 : set - 1);
+            x_half(K_, nv - 1, nv, set == 0 ? 2 : set - 1, set);
             end_half();
             c_last(set);
             end_half();
-            if (fuse_write()) fuse_load();
         }
     }
 
@@ -966,16 +1018,9 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         }
     }
 
-    // the buffers take the output rows once every tile load has landed and
-    // every wave is past its last read (a fused append's FN loads, issued
-    // after each wave's tile loads, stay in flight)
-    const bool fw = fuse_write();
-    if (fw) {
-        if (FN == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
-        wait_vm(0);
-    }
+    // the buffers take the output rows once every load has landed and every
+    // wave is past its last read
+    wait_vm(0);
     wg_barrier();
     if (wave_active) {
         const float l_tot = l_part + __shfl_xor(l_part, 32);
@@ -983,7 +1028,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         T::store_o((char*)smem + wave * WROWS * T::ORS, (__bf16*)a.o + qoff - (size_t)l32 * rs, rsb, oacc,
                    my_valid ? 1.0f / l_tot : 0.0f, lane, tw1 - tw0 + 1);
     }
-    if (fw) fuse_store();
+    if constexpr (FUSE) fuse_tail();
 }
 template <int D>
 hipError_t launch(const PrefillArgs& a, hipStream_t st) {
@@ -991,9 +1036,11 @@ hipError_t launch(const PrefillArgs& a, hipStream_t st) {
     const long long nblk = a.pair_mode ? (long long)a.B * a.Hkv * (G / 2) * a.n_mtiles
                                        : (long long)a.B * a.Hq * a.n_mtiles;
     if (a.ng > 0)
-        hipLaunchKernelGGL((prefill_pp_kernel<D, true>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
+        hipLaunchKernelGGL((prefill_pp_kernel<D, true, false>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
+    else if (a.kc_next != nullptr)
+        hipLaunchKernelGGL((prefill_pp_kernel<D, false, true>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
     else
-        hipLaunchKernelGGL((prefill_pp_kernel<D, false>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
+        hipLaunchKernelGGL((prefill_pp_kernel<D, false, false>), dim3((unsigned)nblk), dim3(PNT), 0, st, a);
     return hipGetLastError();
 }
 
