@@ -158,6 +158,9 @@ def filled_slots(s, r, T):
     (1, 8, 2, 128, 70, 50, 30, 20, 0.0),        # pos0 <= s, L < r: sinks from the cache and the chunk
     (1, 4, 4, 128, 0, 64, 200, 1000, 1e4),      # no sinks
     (1, 6, 2, 128, 4, 28, 517, 4096, 0.0),      # three q-heads per kv-head (256-row halves)
+    (1, 2, 2, 128, 4, 2000, 2100, 5000, 1e4),   # long bands: copy steps every 2nd X half-slot
+    (1, 8, 2, 128, 4, 1500, 1600, 3000, 0.0),   # long bands, GQA pairs
+    (2, 2, 2, 64, 4, 900, 1000, 2000, 1e4),     # long bands, d = 64 (32-row copy steps)
 ])
 def test_prefill_append_equals_separate_calls(gpu, B, Hq, Hkv, d, s, r, L, pos0, rope):
     """swa_prefill_append against swa_prefill + swa_cache_append: the same rows
