@@ -63,6 +63,13 @@ SPILL_OK = {
     # band go to scratch (one reloaded in the masked-tile path); the plain
     # kernel, which every other call runs, has no spill
     "_ZN3swa12_GLOBAL__N_117prefill_pp_kernelILi128ELb1ELb0EEEvNS_11PrefillArgsE",
+    # the bf16 prefill with the fused cache append at d = 128: with the band
+    # walked rotated (one more scalar across the band) the query row's
+    # address and two scalars of the query-reload path go to scratch and VGPR
+    # lanes; that path runs at most once per work item (the switch from the
+    # sink tile to the band without the sink turn), and the launches
+    # measured no slower than without the rotation
+    "_ZN3swa12_GLOBAL__N_117prefill_pp_kernelILi128ELb0ELb1EEEvNS_11PrefillArgsE",
 }
 
 

@@ -423,6 +423,29 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     const int nv = n0 + n1;
     auto phase_of = [&](int v) __attribute__((always_inline)) -> Phase { return v < n0 ? ph0 : ph1; };
     auto tile_of = [&](int v) __attribute__((always_inline)) -> int { return v < n0 ? ph0.first + v : ph1.first + (v - n0); };
+    // The tiles of the last phase are one arithmetic run, key tile vo0 + u
+    // for run index u in [vo, nv).  The band walks that run rotated: step v
+    // takes run index rot(v), the tile whose absolute index is congruent to
+    // v - vo modulo the run's length.  The work items that share K/V (the
+    // query tiles of one kv-head) have runs of one length offset by a few
+    // tiles, so at each step they read the same tile or one of two, which
+    // their XCD's L2 then serves; walked in plain order they would read as
+    // many tiles as there are items, each again several tiles later.  It
+    // also spreads the items' own (last) tiles over the band.
+    const Phase PL = nph >= 2 ? ph1 : ph0;
+    const int vo = nph >= 2 ? n0 : 0;
+    const int vo0 = PL.first - vo;
+    const int nrun = nv - vo;
+    int rho = 0;
+    if (nrun > 1) {
+        rho = PL.first % nrun;
+        rho = rho == 0 ? 0 : nrun - rho;
+    }
+    auto rot = [&](int v) __attribute__((always_inline)) -> int {
+        if (v < vo) return v;
+        const int u = v + rho;
+        return u >= nv ? u - nrun : u;
+    };
 
     // ---- direct loads: a tile's K (or V) is brought in by the 4 waves of
     // one group; wave `sub` issues instructions sub, sub + 4, ...
@@ -448,7 +471,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     auto issue = [&](auto is_k_c, int v, int set) __attribute__((always_inline)) {
         constexpr bool is_k = decltype(is_k_c)::value;
         u32x4* dst0 = is_k ? smem[set].k : smem[set].v;
-        v = v < nv ? v : nv - 1;
+        v = rot(v < nv ? v : nv - 1);
         const Phase P = phase_of(v);
         const int kbase = tile_of(v) * BN, klast = kbase + BN - 1;
         const int lo_any = P.band_lo > t0 - r + 1 ? P.band_lo : t0 - r + 1;
@@ -498,9 +521,9 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     const std::integral_constant<bool, true> K_;
     const std::integral_constant<bool, false> V_;
 
-    // The tiles of the last phase are one arithmetic run, key tile vo0 + v.
-    // Sub-runs are fixed once per work item so the steady state spends a
-    // range check per tile instead of re-deriving the tile's class:
+    // Sub-runs of the last phase's run (in run indices u, see rot) are fixed
+    // once per work item so the steady state spends a range check per tile
+    // instead of re-deriving the tile's class:
     //   [vf_lo, vf_hi]: every row of the tile is needed by some query of the
     //     workgroup and lies in the call's own tokens, so a tile is one
     //     contiguous 16 KB read (the first branch of issue());
@@ -510,9 +533,6 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     //     of the cache.
     // Tiles outside them (sinks, band edges, a tile straddling the cache's
     // wrap) take the general code.
-    const Phase PL = nph >= 2 ? ph1 : ph0;
-    const int vo = nph >= 2 ? n0 : 0;
-    const int vo0 = PL.first - vo;
     auto cdiv = [](int x) __attribute__((always_inline)) { return x >= 0 ? (x + BN - 1) / BN : -((-x) / BN); };
     auto fdiv = [](int x) __attribute__((always_inline)) { return x >= 0 ? x / BN : -((-x + BN - 1) / BN); };
     int vf_lo = 0, vf_hi = -1, vx_lo = 0, vx_hi = -1;
@@ -550,7 +570,7 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // [vc_lo, vc_hi] empty.
     auto issue_run = [&](auto is_k_c, int v, int set) __attribute__((always_inline)) {
         constexpr bool is_k = decltype(is_k_c)::value;
-        const int vv = v < nv ? v : nv - 1;
+        const int vv = rot(v < nv ? v : nv - 1);
         const __bf16* base = nullptr;
         if (vv >= vf_lo && vv <= vf_hi) {
             base = (is_k ? kn : vn) + (size_t)(BN * (vo0 + vv) - pos0) * rs;
@@ -666,8 +686,9 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
         }
         l_part += t;
     };
-    auto cluster_x = [&](int v) __attribute__((always_inline)) {
+    auto cluster_x = [&](int vs) __attribute__((always_inline)) {
         const float NEG = -__builtin_inff();
+        const int v = rot(vs);
         if (v < vx_lo || v > vx_hi) {
             // tiles in [vx_lo, vx_hi] are needed and mask-free for every row
             // of the wave; only the others are classified here (the masks
@@ -818,8 +839,9 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     }
     // X(v)'s copy of tile v (K for group 0, V for group 1) when all its rows
     // are own survivors of the item
-    auto copy_own = [&](int v, int cset) __attribute__((always_inline)) {
+    auto copy_own = [&](int vs, int cset) __attribute__((always_inline)) {
         if constexpr (FUSE) {
+            const int v = rot(vs);
             const int kb = tile_of(v) * BN;
             if (kb + BN - 1 > t1 || kb < t0 || v < vo) return;       // not all own rows (or a sink-phase tile)
             if (__builtin_amdgcn_readfirstlane(finfo.write) == 0) return;
@@ -913,7 +935,8 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // dropped and its weights are zero): the workgroup visits the union of
     // its waves' tiles, and the matrix work saved also lets the clock run
     // higher.
-    auto wave_needs = [&](int v) __attribute__((always_inline)) -> bool {
+    auto wave_needs = [&](int vs) __attribute__((always_inline)) -> bool {
+        const int v = rot(vs);
         if (v >= vx_lo && v <= vx_hi) return true;
         const Phase P = phase_of(v);
         const int kb = tile_of(v) * BN;
