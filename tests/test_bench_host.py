@@ -76,16 +76,19 @@ def test_note_parser_follows_the_kernel_source_hash(tmp_path, monkeypatch):
 
 
 def test_committed_notes_parse():
-    """Every counter note under profiles/ names its kernel sources' hash and
-    carries the figure its kind promises."""
+    """Every counter note under profiles/ carries the figure its kind
+    promises where the bench reads it (a `key: value` line), and was taken
+    on the committed kernel sources (the bench's roofline would otherwise
+    show null for it)."""
     keys = {"traffic": "traffic_bytes_per_launch", "mfma": "mfma_busy_frac", "sclk": "sclk_ghz_timed"}
+    n = 0
     for f in os.listdir(bench.PROFILES):
         m = __import__("re").match(r"(prefill_pp_kernel|decode_split_kernel|backward)_(.+)_(traffic|mfma|sclk)\.md$", f)
         if not m:
             continue
-        text = open(os.path.join(bench.PROFILES, f)).read()
-        assert "kernel_sources_sha256:" in text, f
-        assert keys[m.group(3)] + ":" in text, f
+        assert bench.recorded(m.group(1), m.group(2), m.group(3), keys[m.group(3)]) is not None, f
+        n += 1
+    assert n >= 7
 
 
 def test_bench_refuses_more_than_one_gpu():
