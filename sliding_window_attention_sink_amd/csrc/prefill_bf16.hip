@@ -431,18 +431,20 @@ __global__ __launch_bounds__(PNT) void prefill_pp_kernel(PrefillArgs a) {
     // tiles, so at each step they read the same tile or one of two, which
     // their XCD's L2 then serves; walked in plain order they would read as
     // many tiles as there are items, each again several tiles later.  It
-    // also spreads the items' own (last) tiles over the band.
+    // also spreads the items' own (last) tiles over the band.  The
+    // global-tile instantiation walks in plain order (one more scalar across
+    // its band spills inside the loop there).
     const Phase PL = nph >= 2 ? ph1 : ph0;
     const int vo = nph >= 2 ? n0 : 0;
     const int vo0 = PL.first - vo;
     const int nrun = nv - vo;
     int rho = 0;
-    if (nrun > 1) {
+    if (!GLB && nrun > 1) {
         rho = PL.first % nrun;
         rho = rho == 0 ? 0 : nrun - rho;
     }
     auto rot = [&](int v) __attribute__((always_inline)) -> int {
-        if (v < vo) return v;
+        if (GLB || v < vo) return v;
         const int u = v + rho;
         return u >= nv ? u - nrun : u;
     };
