@@ -644,7 +644,8 @@ def main():
             rooflines["backward_" + wb.name] = {
                 "bound": "mfma", "kernel": "swa_backward (bwd_dq + bwd_dkdv + bwd_reduce kernels)",
                 "achieved": rb["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": rb["tflops"] / PEAK_BF16_TFLOPS, "flops_per_call": rb["flops"], "call_ms": rb["ms"]}
+                "frac": rb["tflops"] / PEAK_BF16_TFLOPS, "flops_per_call": rb["flops"], "call_ms": rb["ms"],
+                "traffic": recorded("backward", wb.name, "traffic", "traffic_bytes_per_launch")}
             log("backward", wb.name, rb)
             torch.cuda.empty_cache()
     if 10 in todo:
