@@ -74,11 +74,15 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BackwardArgs a) {
     const int L = (int)a.L, s = a.s, r = a.r;
     const int G = a.Hq / a.Hkv;
     const int nqt = (L + 127) / 128;
-    // late (heavier) query tiles first; the q-heads of a kv-head adjacent
+    // the q-heads of a kv-head innermost, then the query tiles of that
+    // (batch, kv-head), late (heavier) ones first: each XCD runs the query
+    // tiles of few kv-heads, whose key blocks its L2 then shares
     const int bid = xcd_item(blockIdx.x, gridDim.x);
-    const int qt = nqt - 1 - (bid / a.Hq) % nqt;
-    const int bhq = (bid / (a.Hq * nqt)) * a.Hq + bid % a.Hq;   // b * Hq + h
-    const int b = bhq / a.Hq, h = bhq % a.Hq, kvh = h / G;
+    const int hg = bid % G, rest = bid / G;
+    const int qt = nqt - 1 - rest % nqt;
+    const int bk = rest / nqt;                                   // b * Hkv + kv-head
+    const int b = bk / a.Hkv, kvh = bk % a.Hkv, h = kvh * G + hg;
+    const int bhq = b * a.Hq + h;
     const int t0 = qt * 128, t1 = (t0 + 127) < (L - 1) ? (t0 + 127) : (L - 1);
     const int tw0 = t0 + 32 * wave, tw1 = (tw0 + 31) < t1 ? (tw0 + 31) : t1;
     const bool wave_active = tw0 <= t1;
@@ -120,7 +124,17 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BackwardArgs a) {
         bf = n0;
     }
     const int nv = n0 + n1;
-    auto blk_of = [&](int v) __attribute__((always_inline)) { return v < n0 ? v : bf + (v - n0); };
+    // the band's blocks walked rotated: step v >= n0 takes the band block
+    // whose absolute index is congruent to v - n0 modulo the band's block
+    // count, so the query tiles of a head (bands of one length a few blocks
+    // apart) read the same key block at each step
+    int brho = n1 > 0 ? bf % n1 : 0;
+    brho = brho == 0 ? 0 : n1 - brho;
+    auto blk_of = [&](int v) __attribute__((always_inline)) {
+        if (v < n0) return v;
+        const int u = v - n0 + brho;
+        return bf + (u >= n1 ? u - n1 : u);
+    };
 
     auto issue = [&](int v, int buf) __attribute__((always_inline)) {
         const int kb = blk_of(v) * BLK;
@@ -213,7 +227,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BackwardArgs a) {
 // first the tiles holding sink keys (their queries run to the end), then
 // the others.  Segment seg of a tile walks its query blocks
 // [qb_lo + seg * segb, ...) for every q-head of the kv-head: iteration it
-// is block qb_lo + seg * segb + it / G of q-head kvh * G + it % G.
+// is block qb_lo + seg * segb + qrot(it / G) of q-head kvh * G + it % G
+// (the segment's blocks walked rotated, below).
 //
 // Eight waves in two groups of four share the tile's K and V in LDS; wave
 // (grp, sub) owns keys i0 + 32 sub .. +31 and the iterations it = grp (mod
@@ -294,6 +309,19 @@ __global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, Bwd
     const int sb1 = (sb0 + gr.segb) < nb ? (sb0 + gr.segb) : nb;
     const int niter = (sb1 - sb0) * G;
     const int qbase = (qb_lo + sb0) * BLK;                 // first query of the segment
+    // The segment's query blocks are walked rotated: iteration it takes block
+    // qrot(it / G), the one whose absolute index is congruent to it / G
+    // modulo the segment's block count.  Items of neighbouring key tiles of a
+    // kv-head have segments of one length a few blocks apart, so at each step
+    // they read the same Q and dO block (or one of two), which the XCD's L2
+    // then serves.
+    const int nqb = sb1 - sb0;
+    int qrho = (qb_lo + sb0) % nqb;
+    qrho = qrho == 0 ? 0 : nqb - qrho;
+    auto qrot = [&](int qi) __attribute__((always_inline)) {
+        const int u = qi + qrho;
+        return u >= nqb ? u - nqb : u;
+    };
 
     const int kw0 = i0 + 32 * sub;                         // this wave's keys kw0 .. kw0 + 31
     const int my_key = kw0 + l32;
@@ -312,9 +340,9 @@ __global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, Bwd
 
     // the loads of iteration it into buffer bi, by the four waves of one group
     auto issue = [&](int it, int bi) __attribute__((always_inline)) {
-        const int qi = div_g(it);
-        const int qb = qb_lo + sb0 + qi;
-        const int bhq = b * a.Hq + kvh * G + (it - qi * G);
+        const int q0 = div_g(it);
+        const int qb = qb_lo + sb0 + qrot(q0);
+        const int bhq = b * a.Hq + kvh * G + (it - q0 * G);
         const __bf16* qg = (const __bf16*)a.q + (size_t)bhq * L * D;
         const __bf16* dg = (const __bf16*)a.dout + (size_t)bhq * L * D;
         TT::load(buf_tile(bi, 0), qg, qb * BLK, 0, L - 1, sub, lane);
@@ -330,7 +358,7 @@ __global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, Bwd
     };
     // does this wave's key block meet iteration it's query block?
     auto need_of = [&](int it) __attribute__((always_inline)) {
-        const int tq0 = qbase + BLK * div_g(it);
+        const int tq0 = qbase + BLK * qrot(div_g(it));
         return wave_active && kw0 <= tq0 + BLK - 1 && tq0 <= L - 1 && (kw0 < s || kw0 + BLK - 1 >= tq0 - r + 1);
     };
 
@@ -410,7 +438,7 @@ __global__ __launch_bounds__(2 * NT, 2) void bwd_dkdv_kernel(BackwardArgs a, Bwd
             // ---- X: softmax of iteration h-1, loads of iteration h+2
             const int ix = h - 1;
             if (ix >= 0 && ix < niter && need_of(ix)) {
-                const int tq0 = qbase + BLK * div_g(ix);
+                const int tq0 = qbase + BLK * qrot(div_g(ix));
                 const float* ls = buf_stat(bmod(bh + PB - 1));
                 const float* dd = ls + BLK;
                 // lse and D of this lane's 16 queries (rows 8g .. 8g+7, 16+8g .. +7)
