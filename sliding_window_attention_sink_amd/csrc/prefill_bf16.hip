@@ -23,7 +23,11 @@
 // cluster, so on every SIMD one wave streams MFMAs while the other does the
 // exponentials: a wave never waits for the matrix unit with vector work
 // queued behind its MFMAs.  K and V tiles rotate through three LDS buffer
-// sets and are fetched four clusters before use.
+// sets and are fetched four clusters before use.  "Tile v" is the tile of
+// step v: the band's tiles are walked rotated (the step-v tile is the one
+// whose absolute index is congruent to v modulo the band's tile count), so
+// the work items that share K/V read the same tile at the same step and
+// their XCD's L2 serves it.
 //
 // The 32x32 S^T accumulator gives every lane one query row (lanes l and l+32
 // share it), so the row max is one v_permlane32_swap exchange; K rows enter
