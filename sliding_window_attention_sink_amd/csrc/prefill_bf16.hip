@@ -302,7 +302,9 @@ __device__ __forceinline__ void load_lds16_off(const void* base, uint32_t off, v
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(la) : "m0");
 }
 
-// Wait until at most n of this wave's vector-memory loads are outstanding.
+// Wait until at most n of this wave's vector-memory operations (loads, and
+// the fused copy's stores, which this GPU family counts alike and completes
+// in issue order) are outstanding.
 __device__ __forceinline__ void wait_vm(int n) {
     if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
