@@ -645,7 +645,8 @@ def main():
                 "bound": "mfma", "kernel": "swa_backward (bwd_dq + bwd_dkdv + bwd_reduce kernels)",
                 "achieved": rb["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": rb["tflops"] / PEAK_BF16_TFLOPS, "flops_per_call": rb["flops"], "call_ms": rb["ms"],
-                "traffic": recorded("backward", wb.name, "traffic", "traffic_bytes_per_launch")}
+                "traffic": recorded("backward", wb.name, "traffic", "traffic_bytes_per_launch"),
+                "mfma_busy_frac": recorded("backward", wb.name, "mfma", "mfma_busy_frac")}
             log("backward", wb.name, rb)
             torch.cuda.empty_cache()
     if 10 in todo:
